@@ -1,0 +1,65 @@
+"""Block-scaled W4A4 GEMM reference, GELU-tanh and the FFN chain.
+
+Test infrastructure only (see the package docstring).
+
+The pages replace the BF16 GEMMs of the generator by FP4 GEMMs on both
+weights and activations (tailorednewshub.com "Inferencia W4A4 NVFP4";
+neurohive.io LongLive-2.0 summary, NVFP4 paragraph).  The product of two
+NVFP4 operands quantized along the reduction dimension K is, by definition of
+the format,
+
+    C[m, n] = S_A * S_B * sum_k P_A[m, k] * P_B[n, k],
+    P = e2m1(code) * E4M3(block scale)   (exact),
+
+which is written out here with a float64 matmul over the exactly decoded
+operands.  B is stored [N, K] (K-contiguous, like a linear layer's weight).
+The error bound that parity tests use is
+
+    bound[m, n] = S_A * S_B * sum_k |P_A[m, k] * P_B[n, k]|.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .codec import QTensor, decode_exact, quantize
+
+F32 = np.float32
+
+
+def gemm_ref(a: QTensor, b: QTensor, rows: slice | np.ndarray | None = None):
+    """Return (C, bound) as float64 [M, N] (or the selected rows of A)."""
+    if a.k != b.k:
+        raise ValueError("operands disagree on K")
+    pa = decode_exact(a.codes, a.scales)
+    pb = decode_exact(b.codes, b.scales)
+    if rows is not None:
+        pa = pa[rows]
+    s = float(np.float64(a.tscale[0]) * np.float64(b.tscale[0]))
+    c = (pa @ pb.T) * s
+    bound = (np.abs(pa) @ np.abs(pb).T) * s
+    return c, bound
+
+
+def gelu_tanh(h) -> np.ndarray:
+    """GELU, tanh form: 0.5 h (1 + tanh(sqrt(2/pi) (h + 0.044715 h^3))), in
+    float64.  The pages do not name the FFN activation; this standard form is
+    the reading for the DiT FFN."""
+    h = np.asarray(h, dtype=np.float64)
+    c = np.sqrt(2.0 / np.pi)
+    return 0.5 * h * (1.0 + np.tanh(c * (h + 0.044715 * h ** 3)))
+
+
+def ffn_chain(x: np.ndarray, w1: QTensor, w2: QTensor):
+    """Full-oracle FFN pair: quantize x -> GEMM1 -> GELU -> float32 H ->
+    quantize H (its own global amax) -> GEMM2.
+
+    Returns a dict with every intermediate (float64 GEMM results and bounds,
+    the float32 H and the quantized operands)."""
+    xq = quantize(np.asarray(x, dtype=np.float32))
+    c1, b1 = gemm_ref(xq, w1)
+    h64 = gelu_tanh(c1)
+    h32 = h64.astype(np.float32)
+    hq = quantize(h32)
+    c2, b2 = gemm_ref(hq, w2)
+    return {"xq": xq, "c1": c1, "b1": b1, "h64": h64, "h32": h32, "hq": hq, "c2": c2, "b2": b2}
