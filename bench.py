@@ -1,0 +1,306 @@
+"""Benchmark of the NVFP4 W4A4 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-rows] [--no-cpu]
+
+One step = one pass of the attention-projection workload of the 5B DiT
+(2640 tokens = 3 latent frames x 880, width 3072): amax of the bf16
+activations, their NVFP4 encode, and the block-scaled W4A4 GEMM against
+pre-quantized 3072x3072 NVFP4 weights into bf16.  The timed region starts
+with every input resident in HBM; buffers rotate over 13 independent sets
+(> 512 MB) so the 256 MB Infinity Cache cannot serve a step from the last
+one.  Prints ONE JSON line.
+
+Besides the headline value the line carries:
+  roofline      the GEMM kernel (the dominant kernel), timed with HIP events
+                on its own stream inside the timed region;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same
+                workload on this host;
+  rows          the other rows of the path, each timed the same way: KV codec
+                quantize/dequantize (12x880x24x128 bf16, K and V), RHT16 +
+                quantize of a 16384x3072 gradient along dim 0, the 3072x3072x
+                16384 weight-gradient GEMM, and the FFN pair
+                (10560x3072 -> 14336 -> 3072).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A4 NVFP4 GEMM TFLOPS (incl. act quant) at DiT shapes; quant/KV codec GB/s"
+HBM_PEAK_GBS = 8000.0
+PEAK_TFLOPS = {"f16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-rows", action="store_true", help="skip the per-row extra measurements")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--sets", type=int, default=13, help="rotating buffer sets")
+    return p.parse_args()
+
+
+class Timer:
+    """Pairs of HIP events recorded on one stream around one kernel call."""
+
+    def __init__(self, torch, stream, n):
+        self.torch = torch
+        self.stream = stream
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        self.i = 0
+
+    def start(self):
+        self.ev[self.i][0].record(self.stream)
+
+    def stop(self):
+        self.ev[self.i][1].record(self.stream)
+        self.i += 1
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.ev[: self.i]]))
+
+
+def _dev_bf16(torch, bits):
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def bench_attn_proj(nv, torch, wl, steps, warmup, nsets):
+    d = wl.attn_proj()
+    m, k = d["x"].shape
+    n = d["w"].shape[0]
+    x0 = _dev_bf16(torch, d["x"])
+    w0 = torch.from_numpy(d["w"]).cuda()
+    sets = []
+    for i in range(nsets):
+        x = x0.clone()
+        wq = nv.quantize(w0.clone())  # offline weight quantization (untimed)
+        sets.append({
+            "x": x, "wq": wq,
+            "xq": nv.NVFP4Tensor.empty(m, k, 1, "cuda"),
+            "ws": torch.empty(4, device="cuda"),
+            "y": torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
+        })
+    stream = torch.cuda.current_stream()
+    tq = Timer(torch, stream, steps)
+    tg = Timer(torch, stream, steps)
+
+    def step(s, timed):
+        if timed:
+            tq.start()
+        nv.quantize(s["x"], out=s["xq"], ws=s["ws"], stream=stream)
+        if timed:
+            tq.stop()
+            tg.start()
+        nv.gemm(s["xq"], s["wq"], out=s["y"], stream=stream)
+        if timed:
+            tg.stop()
+
+    for i in range(warmup):
+        step(sets[i % nsets], False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(sets[i % nsets], True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    flops = 2.0 * m * n * k
+    quant_bytes = m * k * 2 + m * k // 2 + m * k // 16 + 4
+    return {
+        "m": m, "n": n, "k": k, "wall_s": wall, "ms_per_step": wall * 1e3 / steps,
+        "gemm_ms": tg.mean_ms(), "quant_ms": tq.mean_ms(), "flops": flops, "quant_bytes": quant_bytes,
+    }
+
+
+def _time_loop(torch, fn, sets, steps, warmup):
+    stream = torch.cuda.current_stream()
+    t = Timer(torch, stream, steps)
+    for i in range(warmup):
+        fn(sets[i % len(sets)], None)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        fn(sets[i % len(sets)], t)
+    torch.cuda.synchronize()
+    return t.mean_ms()
+
+
+def bench_rows(nv, torch, wl, steps, warmup):
+    out = {}
+    stream = torch.cuda.current_stream()
+    # KV codec: K and V [12, 880, 24, 128] bf16, 8-frame blocks.
+    d = wl.kv_cache()
+    shape = (12, 880, 24, 128)
+    kvsets = []
+    for i in range(4):  # 4 sets x (2 x 65 MB in + 2 x 18 MB codes + 2 x 65 MB out) > 256 MB
+        s = {}
+        for nm in ("k", "v"):
+            s[nm] = _dev_bf16(torch, d[nm]).reshape(shape)
+            s[nm + "q"] = nv.NVFP4Tensor.empty(12 * 880 * 24, 128, 2, "cuda")
+            s[nm + "o"] = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        s["ws"] = torch.empty(8, device="cuda")
+        kvsets.append(s)
+
+    def kvq(s, t):
+        if t: t.start()
+        nv.kv_quant(s["k"], out=s["kq"], ws=s["ws"], stream=stream)
+        nv.kv_quant(s["v"], out=s["vq"], ws=s["ws"], stream=stream)
+        if t: t.stop()
+
+    def kvd(s, t):
+        if t: t.start()
+        nv.kv_dequant(s["kq"], shape, out=s["ko"], stream=stream)
+        nv.kv_dequant(s["vq"], shape, out=s["vo"], stream=stream)
+        if t: t.stop()
+
+    elems = 2 * 12 * 880 * 24 * 128
+    kv_bytes = elems * 2 + elems // 2 + elems // 16 + 2 * 2 * 4
+    ms = _time_loop(torch, kvq, kvsets, steps, warmup)
+    out["kv_quant"] = {"ms": ms, "GB/s": kv_bytes / ms / 1e6, "frac_hbm": kv_bytes / ms / 1e6 / HBM_PEAK_GBS,
+                       "bytes": kv_bytes}
+    ms = _time_loop(torch, kvd, kvsets, steps, warmup)
+    out["kv_dequant"] = {"ms": ms, "GB/s": kv_bytes / ms / 1e6, "frac_hbm": kv_bytes / ms / 1e6 / HBM_PEAK_GBS,
+                         "bytes": kv_bytes}
+    del kvsets
+    # RHT16 + quantize along dim 0, and the weight-gradient GEMM.
+    d = wl.rht_wgrad()
+    rows, cols = d["g"].shape
+    rsets = []
+    for i in range(3):
+        s = {"g": _dev_bf16(torch, d["g"]), "x": _dev_bf16(torch, d["x"]),
+             "gq": nv.NVFP4Tensor.empty(cols, rows, 1, "cuda"), "ws": torch.empty(4, device="cuda")}
+        s["xq"] = nv.rht16_quantize(s["x"], d["mask"], axis=0)
+        s["c"] = torch.empty((cols, cols), dtype=torch.float32, device="cuda")
+        rsets.append(s)
+
+    def rq(s, t):
+        if t: t.start()
+        nv.rht16_quantize(s["g"], d["mask"], axis=0, out=s["gq"], ws=s["ws"], stream=stream)
+        if t: t.stop()
+
+    def wg(s, t):
+        if t: t.start()
+        nv.gemm(s["gq"], s["xq"], out=s["c"], stream=stream)
+        if t: t.stop()
+
+    rbytes = rows * cols * 2 + rows * cols // 2 + rows * cols // 16 + 4
+    ms = _time_loop(torch, rq, rsets, steps, warmup)
+    out["rht16_quantize"] = {"ms": ms, "GB/s": rbytes / ms / 1e6, "frac_hbm": rbytes / ms / 1e6 / HBM_PEAK_GBS,
+                             "bytes": rbytes}
+    ms = _time_loop(torch, wg, rsets, max(steps // 2, 5), 3)
+    fl = 2.0 * cols * cols * rows
+    out["wgrad_gemm"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_f16_peak": fl / ms / 1e9 / PEAK_TFLOPS["f16"]}
+    del rsets
+    # FFN pair.
+    d = wl.ffn()
+    m, dm = d["x"].shape
+    f = d["w1"].shape[0]
+    x = _dev_bf16(torch, d["x"])
+    w1 = nv.quantize(torch.from_numpy(d["w1"]).cuda())
+    w2 = nv.quantize(torch.from_numpy(d["w2"]).cuda())
+    bufs = {"xq": nv.NVFP4Tensor.empty(m, dm, 1, "cuda"), "ws": torch.empty(4, device="cuda"),
+            "h": torch.empty((m, f), dtype=torch.float32, device="cuda"),
+            "hmax": torch.empty(1, device="cuda"), "hq": nv.NVFP4Tensor.empty(m, f, 1, "cuda"),
+            "y": torch.empty((m, dm), dtype=torch.bfloat16, device="cuda")}
+
+    def ffn(s, t):
+        if t: t.start()
+        nv.ffn(x, w1, w2, bufs=bufs, stream=stream)
+        if t: t.stop()
+
+    ms = _time_loop(torch, ffn, [None], max(steps // 5, 3), 2)
+    fl = 2.0 * m * dm * f * 2
+    out["ffn_pair"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_f16_peak": fl / ms / 1e9 / PEAK_TFLOPS["f16"]}
+    return out
+
+
+def cpu_baseline(wl):
+    """The oracle, as it stands, on the attention-projection workload: act
+    quantize of the sampled rows + float64 GEMM against the (untimed,
+    pre-quantized) weights."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    d = wl.attn_proj()
+    x = (d["x"].astype(np.uint32) << 16).view(np.float32)
+    wq = oracle.quantize(d["w"])
+    rows = 660  # a quarter of the 2640 tokens
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        xq = oracle.quantize(x[:rows] if reps % 2 == 0 else x[rows:2 * rows])
+        oracle.gemm_ref(xq, wq, want_bound=False)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or reps >= 8:
+            break
+    fl = 2.0 * rows * d["w"].shape[0] * d["w"].shape[1] * reps
+    return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{reps} x (quantize {rows}x3072 bf16 rows + float64 GEMM against 3072x3072 NVFP4 weights), "
+                      f"{el:.1f} s; element-wise codec single-threaded NumPy, GEMM on {blas_threads} BLAS threads"}
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {a.gpus} is not supported by this build "
+              "(the NVFP4 path here has no multi-GPU component)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as wl
+    import nvfp4_w4a4_block_02_amd as nv
+
+    torch.cuda.init()
+    r = bench_attn_proj(nv, torch, wl, a.steps, a.warmup, a.sets)
+    tf = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
+    gemm_tf = r["flops"] / (r["gemm_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(tf, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "dit_attn_proj_2640x3072x3072", "M": r["m"], "N": r["n"], "K": r["k"],
+                   "act_in": "bf16", "weights": "nvfp4 (pre-quantized)", "out": "bf16",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tf, 2), "peak": PEAK_TFLOPS["f16"],
+                     "unit": "TFLOP/s", "frac": round(gemm_tf / PEAK_TFLOPS["f16"], 4), "traffic": None,
+                     "kernel": "gemm_kernel (nvfp4_gemm)", "kernel_ms": round(r["gemm_ms"], 5),
+                     "frac_fp8_peak": round(gemm_tf / PEAK_TFLOPS["fp8"], 4),
+                     "frac_fp4_peak": round(gemm_tf / PEAK_TFLOPS["fp4"], 4)},
+        "act_quant": {"ms": round(r["quant_ms"], 5), "GB/s": round(r["quant_bytes"] / r["quant_ms"] / 1e6, 1),
+                      "frac_hbm": round(r["quant_bytes"] / r["quant_ms"] / 1e6 / HBM_PEAK_GBS, 4)},
+    }
+    if not a.no_rows:
+        rows = bench_rows(nv, torch, wl, max(a.steps // 2, 5), max(a.warmup // 2, 2))
+        line["rows"] = {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                        for k, v in rows.items()}
+    if not a.no_cpu:
+        cb = cpu_baseline(wl)
+        cb["value"] = round(cb["value"], 6)
+        line["cpu_baseline"] = cb
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

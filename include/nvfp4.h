@@ -1,0 +1,205 @@
+/*
+ * nvfp4.h — C ABI of the MI355X (gfx950) NVFP4 W4A4 library (libnvfp4.so).
+ *
+ * Format (what every entry point reads or writes).  NVFP4 stores each element
+ * as a 4-bit E2M1 code (sign, 2 exponent bits, 1 mantissa bit; magnitudes
+ * 0, .5, 1, 1.5, 2, 3, 4, 6), one FP8 block scale per 16 consecutive elements
+ * and one FP32 scale per tensor — neurohive.io, "LongLive-2.0: NVIDIA научила
+ * модель генерировать длинное видео в реальном времени с квантованием NVFP4",
+ * section "Ключевые компоненты LongLive-2.0" (NVFP4 paragraph), and
+ * tailorednewshub.com, "LongLive-2.0: Infraestructura paralela NVFP4 para
+ * video largo", section "Entrenamiento NVFP4" (FP8 block / FP32 tensor
+ * scale).  Readings where the pages are silent, fixed by this library:
+ *
+ *   - the FP8 block scale is OCP E4M3FN (bias 7, max 448, no infinities);
+ *   - domain amax A, tensor scale S = A / 2688 (2688 = 6 * 448);
+ *   - block scale s_b = E4M3_RNE_satfinite((max|x| over the block / 6) / S);
+ *   - element code = sign(x) | E2M1_RNE_satfinite(|x| * (1 / (f32(s_b) * S)));
+ *     a negative value that rounds to zero keeps its sign (code 0x8);
+ *   - all scale arithmetic is IEEE float32 with correctly rounded division;
+ *   - decode: x' = f32(e2m1 * s_b) * S (the first product is exact).
+ *
+ * Memory layout of an NVFP4 tensor of `rows` x `k` (blocks run along k):
+ *   codes  [rows][k/2] bytes, byte j = code[2j] | code[2j+1] << 4;
+ *   scales [rows][k/16] E4M3FN bytes, row-major, no swizzle;
+ *   tscale one float32 S per scaling domain (1 for a plain tensor).
+ * Storage is 4.5 bits per element, i.e. 3.56x smaller than bf16 (the pages
+ * report about 3.6x for the NVFP4 KV cache: tailorednewshub.com, section
+ * "Inferencia W4A4 NVFP4").
+ *
+ * Conventions shared by every entry point:
+ *   - Ownership: the caller owns every buffer (inputs, outputs, workspace).
+ *     The library never allocates or frees memory and keeps no mutable global
+ *     state, so concurrent calls on different streams are safe as long as
+ *     their buffers do not overlap.
+ *   - Pointers named x / c / out / codes / scales / tscale / amax / ws are
+ *     DEVICE pointers; the nvfp4_tensor structs themselves live in HOST memory
+ *     and are read before the call returns.
+ *   - Asynchrony: every call enqueues its kernels on `stream` (a hipStream_t;
+ *     NULL = the default stream) and returns without synchronizing.  Results
+ *     are visible after the caller synchronizes that stream.
+ *   - Errors: argument problems are detected on the host before any HIP call
+ *     and return NVFP4_EINVAL (null pointer, k % 16 != 0, ld < cols,
+ *     misalignment, mismatched operands, unknown dtype/flag); a workspace that
+ *     is too small returns NVFP4_EWORKSPACE; a failed launch returns
+ *     NVFP4_EHIP.  Zero-sized problems return NVFP4_OK without launching.
+ *   - Inputs must be finite.  Non-finite inputs give unspecified codes; there
+ *     is no check on the device.  Tensors whose amax is below about 2^-100
+ *     (where 1/(s_b * S) overflows float32) also give unspecified codes.
+ *   - Alignment: device pointers must be 16-byte aligned; the leading
+ *     dimension of an input (in elements) must keep every row 16-byte aligned
+ *     (bf16: ld % 8 == 0; float32: ld % 4 == 0).
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define NVFP4_OK            0
+#define NVFP4_EINVAL       -1
+#define NVFP4_EUNSUPPORTED -2
+#define NVFP4_EWORKSPACE   -3
+#define NVFP4_EHIP         -4
+
+/* Element types of dense (non-NVFP4) tensors. */
+#define NVFP4_F32  0
+#define NVFP4_BF16 1
+
+/* GEMM epilogues. */
+#define NVFP4_EPI_NONE      0
+#define NVFP4_EPI_GELU_TANH 1
+
+/* Workspace queries (nvfp4_workspace_bytes `op`). */
+#define NVFP4_OP_QUANTIZE 0
+#define NVFP4_OP_RHT16    1
+#define NVFP4_OP_GEMM     2
+#define NVFP4_OP_KV_QUANT 3
+
+/* An NVFP4 tensor (host struct holding device pointers), layout above. */
+typedef struct {
+  uint8_t *codes;   /* device, [rows][k/2]                      */
+  uint8_t *scales;  /* device, [rows][k/16] E4M3FN               */
+  float   *tscale;  /* device, [n_domains] float32 tensor scales */
+  int64_t  rows;
+  int64_t  k;       /* multiple of 16                            */
+} nvfp4_tensor;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int nvfp4_version(void);
+
+/* Human-readable text of a status code (static string, never NULL). */
+const char *nvfp4_status_string(int status);
+
+/* Bytes of device workspace `op` needs for a rows x cols problem (for
+ * NVFP4_OP_KV_QUANT: rows = frames, cols = frame_block).  The workspace
+ * must be 16-byte aligned; its contents on entry do not matter. */
+size_t nvfp4_workspace_bytes(int op, int64_t rows, int64_t cols);
+
+/*
+ * Domain amax (step 1 of the recipe): amax[d] = max |x| over the rows of
+ * domain d, where domain d is rows [d*rows_per_domain, (d+1)*rows_per_domain)
+ * (the last domain may be shorter; rows_per_domain = 0 means one domain).
+ * x: device [rows][ld] of `dtype`.  amax: device float32
+ * [ceil(rows/rows_per_domain)], overwritten.
+ */
+int nvfp4_amax(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+               int64_t rows_per_domain, float *amax, void *stream);
+
+/*
+ * Encode (steps 2-6) given each domain's amax: writes codes, block scales
+ * and tscale[d] = amax[d] / 2688.
+ *   axis = 1: blocks run along cols (x is [rows][cols], K-contiguous); the
+ *             output is rows x cols.
+ *   axis = 0: blocks run along rows (x's reduction dim is dim 0, as for a
+ *             weight gradient); the output is stored transposed, cols x rows,
+ *             and rows_per_domain must be 0.
+ * `out` must describe the output shape exactly; out->tscale needs one float
+ * per domain.
+ */
+int nvfp4_encode(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                 int axis, int64_t rows_per_domain, const float *amax,
+                 const nvfp4_tensor *out, void *stream);
+
+/*
+ * Quantize a whole tensor (one domain): nvfp4_amax into the workspace, then
+ * nvfp4_encode.  ws: device, >= nvfp4_workspace_bytes(NVFP4_OP_QUANTIZE, ...).
+ * This is the activation (and offline weight) quantizer of the W4A4 linear
+ * layers (tailorednewshub.com, section "Inferencia W4A4 NVFP4").
+ */
+int nvfp4_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                   int axis, const nvfp4_tensor *out, void *ws, size_t ws_bytes,
+                   void *stream);
+
+/*
+ * Random Hadamard transform then quantize (gradient path: the pages apply an
+ * RHT before quantizing weight gradients — neurohive.io NVFP4 paragraph;
+ * tailorednewshub.com, "Entrenamiento NVFP4").  Every 16-element block v
+ * along `axis` becomes v' = (1/4) * H16 * diag(d) * v, with H16 the Sylvester
+ * Hadamard matrix and d_j = -1 iff bit j of sign_mask is set (one mask for
+ * the whole tensor), evaluated in float32 as: sign flip, butterfly stages of
+ * stride 1, 2, 4, 8 ((a, b) -> (a + b, a - b)), multiply by 0.25.  The amax
+ * and all scales are those of the transformed tensor.  Axis and layout as in
+ * nvfp4_encode.  ws: >= nvfp4_workspace_bytes(NVFP4_OP_RHT16, ...).
+ */
+int rht16_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                   int axis, uint32_t sign_mask, const nvfp4_tensor *out,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Block-scaled W4A4 GEMM (tailorednewshub.com, "Inferencia W4A4 NVFP4": FP4
+ * GEMMs replace BF16 GEMMs):
+ *   c[m][n] = epi( S_A * S_B * sum_k P_A[m][k] * P_B[n][k] ),
+ *   P = e2m1(code) * f32(s_b)  (decoded exactly), float32 accumulation.
+ * a: M x K (a->rows = M), b: N x K (b->rows = N, a linear layer's weight),
+ * both with one tscale.  c: device [M][ldc] of c_dtype (float32 or bf16,
+ * round-to-nearest-even), ldc >= N.  epilogue: NVFP4_EPI_NONE or
+ * NVFP4_EPI_GELU_TANH (0.5 h (1 + tanh(0.79788456 (h + 0.044715 h^3))),
+ * float32).  amax_out: NULL, or a device float that receives max |c| over the
+ * stored values (it is reset by the call), so that c can be re-quantized with
+ * nvfp4_encode without another pass over it.  ws may be NULL
+ * (nvfp4_workspace_bytes(NVFP4_OP_GEMM, ...) is 0).
+ */
+int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype,
+               int64_t ldc, int epilogue, float *amax_out, void *ws, size_t ws_bytes,
+               void *stream);
+
+/*
+ * KV-cache quantization in frame blocks (hyper.ai summary of the LongLive-2.0
+ * paper, section "方法": the KV cache is quantized per block of eight frames).
+ * kv: device bf16 [frames][tokens][heads][head_dim], contiguous.  One tscale
+ * per frame block (frames [b*frame_block, (b+1)*frame_block), the last block
+ * may be partial) over all its tokens and heads; 16-element blocks along
+ * head_dim.  out: rows = frames*tokens*heads, k = head_dim, tscale holds
+ * ceil(frames/frame_block) floats.
+ * ws: >= nvfp4_workspace_bytes(NVFP4_OP_KV_QUANT, frames, frame_block).
+ */
+int nvfp4_kv_quant(const void *kv, int64_t frames, int64_t tokens, int64_t heads,
+                   int64_t head_dim, int64_t frame_block, const nvfp4_tensor *out,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * KV-cache dequantization of the whole window to bf16 (the pages rebuild the
+ * cache with a parallel dequant kernel for window attention: hyper.ai
+ * summary, section "方法").  out: device bf16 [frames][tokens][heads][head_dim].
+ */
+int nvfp4_kv_dequant(const nvfp4_tensor *in, int64_t frames, int64_t tokens, int64_t heads,
+                     int64_t head_dim, int64_t frame_block, void *out, void *stream);
+
+/*
+ * Plain dequantization (decode step), float32 or bf16 output [rows][k],
+ * contiguous; rows_per_domain as in nvfp4_amax (0 = one domain).
+ */
+int nvfp4_dequantize(const nvfp4_tensor *in, int64_t rows_per_domain, void *out,
+                     int dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,0 +1,275 @@
+"""Thin Python binding of libnvfp4.so (MI355X / gfx950 NVFP4 W4A4 path).
+
+Every function here only marshals arguments: it allocates the output tensors
+with torch (device memory is torch's), passes raw device pointers and the
+current HIP stream to the C ABI declared in ``include/nvfp4.h``, and turns a
+non-zero status into an exception.  All arithmetic runs in the HIP kernels.
+
+The library must have been built (``python -m nvfp4_w4a4_block_02_amd.build``);
+importing this module raises if it is missing — there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libnvfp4.so")
+
+F32, BF16 = 0, 1
+EPI_NONE, EPI_GELU_TANH = 0, 1
+OP_QUANTIZE, OP_RHT16, OP_GEMM, OP_KV_QUANT = 0, 1, 2, 3
+
+
+class NVFP4Error(RuntimeError):
+    pass
+
+
+class _CTensor(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("tscale", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("k", ctypes.c_int64),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m nvfp4_w4a4_block_02_amd.build` "
+            "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64, SZ, U32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_uint32
+    TP = ctypes.POINTER(_CTensor)
+    sigs = {
+        "nvfp4_version": (I, []),
+        "nvfp4_status_string": (ctypes.c_char_p, [I]),
+        "nvfp4_workspace_bytes": (SZ, [I, I64, I64]),
+        "nvfp4_amax": (I, [P, I, I64, I64, I64, I64, P, P]),
+        "nvfp4_encode": (I, [P, I, I64, I64, I64, I, I64, P, TP, P]),
+        "nvfp4_quantize": (I, [P, I, I64, I64, I64, I, TP, P, SZ, P]),
+        "rht16_quantize": (I, [P, I, I64, I64, I64, I, U32, TP, P, SZ, P]),
+        "nvfp4_gemm": (I, [TP, TP, P, I, I64, I, P, P, SZ, P]),
+        "nvfp4_kv_quant": (I, [P, I64, I64, I64, I64, I64, TP, P, SZ, P]),
+        "nvfp4_kv_dequant": (I, [TP, I64, I64, I64, I64, I64, P, P]),
+        "nvfp4_dequantize": (I, [TP, I64, P, I, P]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+EXPORTED = ("nvfp4_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_amax",
+            "nvfp4_encode", "nvfp4_quantize", "rht16_quantize", "nvfp4_gemm", "nvfp4_kv_quant",
+            "nvfp4_kv_dequant", "nvfp4_dequantize")
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise NVFP4Error(f"{what}: {lib.nvfp4_status_string(status).decode()} ({status})")
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+@dataclass
+class NVFP4Tensor:
+    """Device NVFP4 tensor: codes [rows, k/2] uint8, scales [rows, k/16] uint8
+    (E4M3FN), tscale [n_domains] float32."""
+
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tscale: torch.Tensor
+
+    @property
+    def rows(self) -> int:
+        return self.codes.shape[0]
+
+    @property
+    def k(self) -> int:
+        return self.codes.shape[1] * 2
+
+    def c(self) -> _CTensor:
+        return _CTensor(self.codes.data_ptr(), self.scales.data_ptr(), self.tscale.data_ptr(), self.rows, self.k)
+
+    @staticmethod
+    def empty(rows: int, k: int, n_domains: int = 1, device="cuda") -> "NVFP4Tensor":
+        return NVFP4Tensor(
+            torch.empty((rows, k // 2), dtype=torch.uint8, device=device),
+            torch.empty((rows, k // 16), dtype=torch.uint8, device=device),
+            torch.empty((max(n_domains, 1),), dtype=torch.float32, device=device),
+        )
+
+
+def workspace_bytes(op: int, rows: int, cols: int) -> int:
+    return int(lib.nvfp4_workspace_bytes(op, rows, cols))
+
+
+def _workspace(op, rows, cols, device):
+    n = max(workspace_bytes(op, rows, cols), 16)
+    return torch.empty((n // 4,), dtype=torch.float32, device=device)
+
+
+def _ld(x: torch.Tensor) -> int:
+    """Leading dimension of a row-major 2-D tensor (a single row may carry any
+    stride in torch; it is then reported as the row length)."""
+    if x.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    if x.shape[1] > 1 and x.stride(1) != 1:
+        raise ValueError("rows must be contiguous (stride 1 along the last dim)")
+    return x.stride(0) if x.shape[0] > 1 else x.shape[1]
+
+
+def _out_shape(x: torch.Tensor, axis: int):
+    rows, cols = x.shape
+    return (rows, cols) if axis == 1 else (cols, rows)
+
+
+def amax(x: torch.Tensor, rows_per_domain: int = 0, out: torch.Tensor | None = None, stream=None):
+    rows, cols = x.shape
+    nd = 1 if rows_per_domain <= 0 or rows_per_domain >= rows else -(-rows // rows_per_domain)
+    if out is None:
+        out = torch.empty((nd,), dtype=torch.float32, device=x.device)
+    _check(lib.nvfp4_amax(_ptr(x), _dtype_code(x), rows, cols, _ld(x), rows_per_domain, _ptr(out),
+                          _stream(stream)), "nvfp4_amax")
+    return out
+
+
+def encode(x: torch.Tensor, amax_t: torch.Tensor, axis: int = 1, rows_per_domain: int = 0,
+           out: NVFP4Tensor | None = None, stream=None) -> NVFP4Tensor:
+    rows, cols = x.shape
+    if out is None:
+        r, k = _out_shape(x, axis)
+        out = NVFP4Tensor.empty(r, k, amax_t.numel(), x.device)
+    ct = out.c()
+    _check(lib.nvfp4_encode(_ptr(x), _dtype_code(x), rows, cols, _ld(x), axis, rows_per_domain,
+                            _ptr(amax_t), ctypes.byref(ct), _stream(stream)), "nvfp4_encode")
+    return out
+
+
+def quantize(x: torch.Tensor, axis: int = 1, out: NVFP4Tensor | None = None, ws: torch.Tensor | None = None,
+             stream=None) -> NVFP4Tensor:
+    rows, cols = x.shape
+    if out is None:
+        r, k = _out_shape(x, axis)
+        out = NVFP4Tensor.empty(r, k, 1, x.device)
+    if ws is None:
+        ws = _workspace(OP_QUANTIZE, rows, cols, x.device)
+    ct = out.c()
+    _check(lib.nvfp4_quantize(_ptr(x), _dtype_code(x), rows, cols, _ld(x), axis, ctypes.byref(ct),
+                              _ptr(ws), ws.numel() * 4, _stream(stream)), "nvfp4_quantize")
+    return out
+
+
+def rht16_quantize(x: torch.Tensor, sign_mask: int, axis: int = 1, out: NVFP4Tensor | None = None,
+                   ws: torch.Tensor | None = None, stream=None) -> NVFP4Tensor:
+    rows, cols = x.shape
+    if out is None:
+        r, k = _out_shape(x, axis)
+        out = NVFP4Tensor.empty(r, k, 1, x.device)
+    if ws is None:
+        ws = _workspace(OP_RHT16, rows, cols, x.device)
+    ct = out.c()
+    _check(lib.rht16_quantize(_ptr(x), _dtype_code(x), rows, cols, _ld(x), axis, sign_mask,
+                              ctypes.byref(ct), _ptr(ws), ws.numel() * 4, _stream(stream)), "rht16_quantize")
+    return out
+
+
+def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.bfloat16, epilogue: int = EPI_NONE,
+         amax_out: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((a.rows, b.rows), dtype=out_dtype, device=a.codes.device)
+    ca, cb = a.c(), b.c()
+    _check(lib.nvfp4_gemm(ctypes.byref(ca), ctypes.byref(cb), _ptr(out), _dtype_code(out), _ld(out),
+                          epilogue, _ptr(amax_out), None, 0, _stream(stream)), "nvfp4_gemm")
+    return out
+
+
+def kv_quant(kv: torch.Tensor, frame_block: int = 8, out: NVFP4Tensor | None = None,
+             ws: torch.Tensor | None = None, stream=None) -> NVFP4Tensor:
+    f, t, h, d = kv.shape
+    if kv.dtype != torch.bfloat16 or not kv.is_contiguous():
+        raise TypeError("kv must be a contiguous bfloat16 tensor [frames, tokens, heads, head_dim]")
+    nd = -(-f // frame_block)
+    if out is None:
+        out = NVFP4Tensor.empty(f * t * h, d, nd, kv.device)
+    if ws is None:
+        ws = _workspace(OP_KV_QUANT, f, frame_block, kv.device)
+    ct = out.c()
+    _check(lib.nvfp4_kv_quant(_ptr(kv), f, t, h, d, frame_block, ctypes.byref(ct), _ptr(ws), ws.numel() * 4,
+                              _stream(stream)), "nvfp4_kv_quant")
+    return out
+
+
+def kv_dequant(q: NVFP4Tensor, shape, frame_block: int = 8, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    f, t, h, d = shape
+    if out is None:
+        out = torch.empty((f, t, h, d), dtype=torch.bfloat16, device=q.codes.device)
+    ct = q.c()
+    _check(lib.nvfp4_kv_dequant(ctypes.byref(ct), f, t, h, d, frame_block, _ptr(out), _stream(stream)),
+           "nvfp4_kv_dequant")
+    return out
+
+
+def dequantize(q: NVFP4Tensor, dtype=torch.float32, rows_per_domain: int = 0, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((q.rows, q.k), dtype=dtype, device=q.codes.device)
+    ct = q.c()
+    _check(lib.nvfp4_dequantize(ctypes.byref(ct), rows_per_domain, _ptr(out), _dtype_code(out), _stream(stream)),
+           "nvfp4_dequantize")
+    return out
+
+
+def linear(x: torch.Tensor, w: NVFP4Tensor, out_dtype=torch.bfloat16, xq: NVFP4Tensor | None = None,
+           ws: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """W4A4 linear layer: quantize the activations, then the block-scaled GEMM
+    against pre-quantized weights w [N, K]."""
+    xq = quantize(x, axis=1, out=xq, ws=ws, stream=stream)
+    return gemm(xq, w, out_dtype=out_dtype, out=out, stream=stream)
+
+
+def ffn(x: torch.Tensor, w1: NVFP4Tensor, w2: NVFP4Tensor, out_dtype=torch.bfloat16, bufs: dict | None = None,
+        stream=None) -> torch.Tensor:
+    """DiT FFN pair on NVFP4: quantize x -> GEMM1 with GELU-tanh epilogue into
+    float32 H (the epilogue also reduces max|H|) -> re-quantize H with that
+    amax -> GEMM2."""
+    m = x.shape[0]
+    dev = x.device
+    if bufs is None:
+        bufs = {}
+    xq = quantize(x, out=bufs.get("xq"), ws=bufs.get("ws"), stream=stream)
+    h = bufs.get("h")
+    if h is None:
+        h = torch.empty((m, w1.rows), dtype=torch.float32, device=dev)
+    hmax = bufs.get("hmax")
+    if hmax is None:
+        hmax = torch.empty((1,), dtype=torch.float32, device=dev)
+    gemm(xq, w1, epilogue=EPI_GELU_TANH, amax_out=hmax, out=h, stream=stream)
+    hq = encode(h, hmax, out=bufs.get("hq"), stream=stream)
+    return gemm(hq, w2, out_dtype=out_dtype, out=bufs.get("y"), stream=stream)

@@ -1,0 +1,206 @@
+// C ABI of libnvfp4.so: argument validation (host only, before any HIP call)
+// and kernel launches on the caller's stream.  See include/nvfp4.h for the
+// contract of every entry point.
+#include "../../include/nvfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+constexpr int64_t kMaxBlocks = (int64_t)1 << 31;  // kernels index 16-element blocks with 32 bits
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_dtype(int dt) { return dt == NVFP4_F32 || dt == NVFP4_BF16; }
+
+int64_t elem_size(int dt) { return dt == NVFP4_F32 ? 4 : 2; }
+
+// Rows stay 16-byte aligned when ld * elem_size is a multiple of 16.
+bool ld_ok(int64_t ld, int dt) { return (ld * elem_size(dt)) % 16 == 0; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP; }
+
+bool tensor_ok(const nvfp4_tensor* t) {
+  return t && t->codes && t->scales && t->tscale && aligned16(t->codes) && aligned16(t->scales) &&
+         aligned16(t->tscale) && t->rows >= 0 && t->k >= 0 && t->k % 16 == 0;
+}
+
+int64_t ndomains(int64_t rows, int64_t rpd) {
+  if (rpd <= 0 || rpd > rows) return rows > 0 ? 1 : 0;
+  return (rows + rpd - 1) / rpd;
+}
+
+nvfp4::QOut qout(const nvfp4_tensor* t) { return nvfp4::QOut{t->codes, t->scales, t->tscale}; }
+
+// Shared checks of a dense input and its NVFP4 output for axis 0 or 1.
+int check_dense_to_q(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld, int axis,
+                     const nvfp4_tensor* out) {
+  if (!x || !valid_dtype(dt) || rows < 0 || cols < 0 || ld < cols || !aligned16(x) || !ld_ok(ld, dt))
+    return NVFP4_EINVAL;
+  if (!tensor_ok(out)) return NVFP4_EINVAL;
+  if (axis == 1) {
+    if (cols % 16 != 0 || out->rows != rows || out->k != cols) return NVFP4_EINVAL;
+  } else if (axis == 0) {
+    if (rows % 16 != 0 || out->rows != cols || out->k != rows) return NVFP4_EINVAL;
+  } else {
+    return NVFP4_EINVAL;
+  }
+  if ((rows / 16 + 1) * (cols + 1) > kMaxBlocks || rows * (cols / 16 + 1) > kMaxBlocks) return NVFP4_EUNSUPPORTED;
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_version(void) { return kVersion; }
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_EINVAL: return "invalid argument";
+    case NVFP4_EUNSUPPORTED: return "unsupported problem size";
+    case NVFP4_EWORKSPACE: return "workspace too small";
+    case NVFP4_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t nvfp4_workspace_bytes(int op, int64_t rows, int64_t cols) {
+  switch (op) {
+    case NVFP4_OP_QUANTIZE:
+    case NVFP4_OP_RHT16:
+      return 16;  // one float32 amax, padded to the alignment
+    case NVFP4_OP_GEMM:
+      return 0;
+    case NVFP4_OP_KV_QUANT: {
+      const int64_t nd = ndomains(rows, cols);
+      return (size_t)((nd * 4 + 15) / 16 * 16);
+    }
+    default:
+      return 0;
+  }
+}
+
+int nvfp4_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+               int64_t rows_per_domain, float* amax, void* stream) {
+  if (!x || !amax || !valid_dtype(dtype) || rows < 0 || cols < 0 || cols % 16 != 0 || ld < cols ||
+      !aligned16(x) || !ld_ok(ld, dtype) || rows_per_domain < 0)
+    return NVFP4_EINVAL;
+  if (rows * (cols / 16) >= kMaxBlocks) return NVFP4_EUNSUPPORTED;
+  if (rows == 0) return NVFP4_OK;
+  if (cols == 0) return from_hip(nvfp4::launch_zero(amax, ndomains(rows, rows_per_domain), (hipStream_t)stream));
+  return from_hip(nvfp4::launch_amax_rows(x, dtype, rows, cols, ld, rows_per_domain, amax, false, 0,
+                                          (hipStream_t)stream));
+}
+
+int nvfp4_encode(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int axis,
+                 int64_t rows_per_domain, const float* amax, const nvfp4_tensor* out, void* stream) {
+  if (!amax || rows_per_domain < 0) return NVFP4_EINVAL;
+  int st = check_dense_to_q(x, dtype, rows, cols, ld, axis, out);
+  if (st != NVFP4_OK) return st;
+  if (axis == 0 && rows_per_domain != 0) return NVFP4_EINVAL;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (axis == 1)
+    return from_hip(nvfp4::launch_encode_rows(x, dtype, rows, cols, ld, rows_per_domain, amax, qout(out), false, 0, s));
+  return from_hip(nvfp4::launch_encode_cols(x, dtype, rows, cols, ld, amax, qout(out), false, 0, s));
+}
+
+static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int axis,
+                         bool rht, uint32_t mask, const nvfp4_tensor* out, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int st = check_dense_to_q(x, dtype, rows, cols, ld, axis, out);
+  if (st != NVFP4_OK) return st;
+  if (rht && mask > 0xFFFFu) return NVFP4_EINVAL;
+  if (!ws || !aligned16(ws)) return NVFP4_EINVAL;
+  if (ws_bytes < nvfp4_workspace_bytes(NVFP4_OP_QUANTIZE, rows, cols)) return NVFP4_EWORKSPACE;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  float* amax = static_cast<float*>(ws);
+  hipError_t e;
+  if (axis == 1 || !rht) {
+    // Without the transform the amax does not depend on the block direction.
+    e = nvfp4::launch_amax_rows(x, dtype, rows, cols, ld, 0, amax, rht && axis == 1, mask, s);
+  } else {
+    e = nvfp4::launch_amax_cols_rht(x, dtype, rows, cols, ld, amax, mask, s);
+  }
+  if (e != hipSuccess) return NVFP4_EHIP;
+  if (axis == 1) e = nvfp4::launch_encode_rows(x, dtype, rows, cols, ld, 0, amax, qout(out), rht, mask, s);
+  else e = nvfp4::launch_encode_cols(x, dtype, rows, cols, ld, amax, qout(out), rht, mask, s);
+  return from_hip(e);
+}
+
+int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int axis,
+                   const nvfp4_tensor* out, void* ws, size_t ws_bytes, void* stream) {
+  return quantize_impl(x, dtype, rows, cols, ld, axis, false, 0, out, ws, ws_bytes, stream);
+}
+
+int rht16_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int axis,
+                   uint32_t sign_mask, const nvfp4_tensor* out, void* ws, size_t ws_bytes, void* stream) {
+  return quantize_impl(x, dtype, rows, cols, ld, axis, true, sign_mask, out, ws, ws_bytes, stream);
+}
+
+int nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int c_dtype, int64_t ldc,
+               int epilogue, float* amax_out, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!tensor_ok(a) || !tensor_ok(b) || !c || !valid_dtype(c_dtype)) return NVFP4_EINVAL;
+  if (a->k != b->k || ldc < b->rows || !aligned16(c)) return NVFP4_EINVAL;
+  if (epilogue != NVFP4_EPI_NONE && epilogue != NVFP4_EPI_GELU_TANH) return NVFP4_EINVAL;
+  if (amax_out && ((uintptr_t)amax_out & 3u)) return NVFP4_EINVAL;
+  if (a->rows >= ((int64_t)1 << 31) || b->rows >= ((int64_t)1 << 31) || a->k >= ((int64_t)1 << 31))
+    return NVFP4_EUNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  if (a->rows == 0 || b->rows == 0) {
+    return amax_out ? from_hip(nvfp4::launch_zero(amax_out, 1, s)) : NVFP4_OK;
+  }
+  return from_hip(nvfp4::launch_gemm(qout(a), qout(b), a->rows, b->rows, a->k, c, c_dtype, ldc, epilogue,
+                                     amax_out, s));
+}
+
+int nvfp4_kv_quant(const void* kv, int64_t frames, int64_t tokens, int64_t heads, int64_t head_dim,
+                   int64_t frame_block, const nvfp4_tensor* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!kv || !aligned16(kv) || frames < 0 || tokens < 0 || heads < 0 || head_dim < 0 || head_dim % 16 != 0 ||
+      frame_block <= 0)
+    return NVFP4_EINVAL;
+  const int64_t rows = frames * tokens * heads;
+  if (!tensor_ok(out) || out->rows != rows || out->k != head_dim) return NVFP4_EINVAL;
+  if (!ws || !aligned16(ws)) return NVFP4_EINVAL;
+  if (ws_bytes < nvfp4_workspace_bytes(NVFP4_OP_KV_QUANT, frames, frame_block)) return NVFP4_EWORKSPACE;
+  if (rows * (head_dim / 16 + 1) >= kMaxBlocks) return NVFP4_EUNSUPPORTED;
+  if (rows == 0 || head_dim == 0) return NVFP4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t rpd = frame_block * tokens * heads;
+  float* amax = static_cast<float*>(ws);
+  hipError_t e = nvfp4::launch_amax_rows(kv, NVFP4_BF16, rows, head_dim, head_dim, rpd, amax, false, 0, s);
+  if (e != hipSuccess) return NVFP4_EHIP;
+  return from_hip(nvfp4::launch_encode_rows(kv, NVFP4_BF16, rows, head_dim, head_dim, rpd, amax, qout(out),
+                                            false, 0, s));
+}
+
+int nvfp4_kv_dequant(const nvfp4_tensor* in, int64_t frames, int64_t tokens, int64_t heads, int64_t head_dim,
+                     int64_t frame_block, void* out, void* stream) {
+  if (!tensor_ok(in) || !out || !aligned16(out) || frames < 0 || tokens < 0 || heads < 0 || frame_block <= 0)
+    return NVFP4_EINVAL;
+  const int64_t rows = frames * tokens * heads;
+  if (in->rows != rows || in->k != head_dim) return NVFP4_EINVAL;
+  if (rows * (head_dim / 16 + 1) >= kMaxBlocks) return NVFP4_EUNSUPPORTED;
+  if (rows == 0 || head_dim == 0) return NVFP4_OK;
+  return from_hip(nvfp4::launch_dequant(qout(in), rows, head_dim, frame_block * tokens * heads, out, NVFP4_BF16,
+                                        (hipStream_t)stream));
+}
+
+int nvfp4_dequantize(const nvfp4_tensor* in, int64_t rows_per_domain, void* out, int dtype, void* stream) {
+  if (!tensor_ok(in) || !out || !aligned16(out) || !valid_dtype(dtype) || rows_per_domain < 0)
+    return NVFP4_EINVAL;
+  if (in->rows * (in->k / 16 + 1) >= kMaxBlocks) return NVFP4_EUNSUPPORTED;
+  if (in->rows == 0 || in->k == 0) return NVFP4_OK;
+  return from_hip(nvfp4::launch_dequant(qout(in), in->rows, in->k, rows_per_domain, out, dtype,
+                                        (hipStream_t)stream));
+}
+
+}  // extern "C"

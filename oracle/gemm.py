@@ -27,17 +27,18 @@ from .codec import QTensor, decode_exact, quantize
 F32 = np.float32
 
 
-def gemm_ref(a: QTensor, b: QTensor, rows: slice | np.ndarray | None = None):
-    """Return (C, bound) as float64 [M, N] (or the selected rows of A)."""
+def gemm_ref(a: QTensor, b: QTensor, rows: slice | np.ndarray | None = None, want_bound: bool = True):
+    """Return (C, bound) as float64 [M, N] (or the selected rows of A); the
+    bound is None when ``want_bound`` is False."""
     if a.k != b.k:
         raise ValueError("operands disagree on K")
+    if rows is not None:
+        a = QTensor(a.codes[rows], a.scales[rows], a.tscale)
     pa = decode_exact(a.codes, a.scales)
     pb = decode_exact(b.codes, b.scales)
-    if rows is not None:
-        pa = pa[rows]
     s = float(np.float64(a.tscale[0]) * np.float64(b.tscale[0]))
     c = (pa @ pb.T) * s
-    bound = (np.abs(pa) @ np.abs(pb).T) * s
+    bound = (np.abs(pa) @ np.abs(pb).T) * s if want_bound else None
     return c, bound
 
 

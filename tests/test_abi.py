@@ -1,0 +1,141 @@
+"""The C ABI library loads on a CPU-only machine, exports every entry point
+include/nvfp4.h declares, and rejects bad arguments on the host before any
+HIP call (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def nv():
+    from nvfp4_w4a4_block_02_amd import build as b
+
+    if not os.path.exists(b.LIB):
+        b.build()
+    import nvfp4_w4a4_block_02_amd as nv
+
+    return nv
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "nvfp4.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char)\s*\*?\s*([a-z0-9_]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(nv):
+    declared = _declared()
+    assert len(declared) >= 11
+    assert sorted(nv.EXPORTED) == declared
+    for name in declared:
+        assert hasattr(nv.lib, name), name
+
+
+def test_version_and_status_strings(nv):
+    assert nv.lib.nvfp4_version() == 10000
+    for code, text in [(0, b"ok"), (-1, b"invalid argument"), (-3, b"workspace too small"), (-4, b"HIP launch failed")]:
+        assert nv.lib.nvfp4_status_string(code) == text
+    assert nv.lib.nvfp4_status_string(123) == b"unknown status"
+
+
+def test_workspace_sizes(nv):
+    assert nv.workspace_bytes(nv.OP_QUANTIZE, 10, 32) == 16
+    assert nv.workspace_bytes(nv.OP_GEMM, 10, 32) == 0
+    assert nv.workspace_bytes(nv.OP_KV_QUANT, 12, 8) == 16      # two frame blocks
+    assert nv.workspace_bytes(nv.OP_KV_QUANT, 40, 8) == 32      # five frame blocks
+
+
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced
+
+
+def _t(nv, rows, k, codes=FAKE, scales=FAKE, tscale=FAKE):
+    return nv._CTensor(codes, scales, tscale, rows, k)
+
+
+def _stream():
+    return ctypes.c_void_p(0)
+
+
+def test_quantize_rejects_bad_arguments(nv):
+    q = nv.lib.nvfp4_quantize
+    ws = ctypes.c_void_p(FAKE)
+    good = _t(nv, 4, 32)
+    EINVAL, EWS = -1, -3
+    # null input, bad dtype, k % 16, ld < cols, misaligned x, bad axis, shape mismatch
+    assert q(None, 1, 4, 32, 32, 1, ctypes.byref(good), ws, 16, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 7, 4, 32, 32, 1, ctypes.byref(good), ws, 16, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 40, 40, 1, ctypes.byref(_t(nv, 4, 40)), ws, 16, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 16, 1, ctypes.byref(good), ws, 16, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE + 2), 1, 4, 32, 32, 1, ctypes.byref(good), ws, 16, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 36, 1, ctypes.byref(good), ws, 16, _stream()) == EINVAL  # row pitch
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 2, ctypes.byref(good), ws, 16, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 1, ctypes.byref(_t(nv, 5, 32)), ws, 16, _stream()) == EINVAL
+    # axis 0 needs rows % 16 and a transposed output
+    assert q(ctypes.c_void_p(FAKE), 1, 20, 32, 32, 0, ctypes.byref(_t(nv, 32, 20)), ws, 16, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 32, 48, 48, 0, ctypes.byref(_t(nv, 32, 48)), ws, 16, _stream()) == EINVAL
+    # null / misaligned output pointers
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 1, ctypes.byref(_t(nv, 4, 32, codes=0)), ws, 16, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 1, ctypes.byref(_t(nv, 4, 32, scales=FAKE + 1)), ws, 16, _stream()) == EINVAL
+    # workspace
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 1, ctypes.byref(good), None, 16, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 1, ctypes.byref(good), ws, 8, _stream()) == EWS
+    # zero-sized problems are a no-op (no launch)
+    assert q(ctypes.c_void_p(FAKE), 1, 0, 32, 32, 1, ctypes.byref(_t(nv, 0, 32)), ws, 16, _stream()) == 0
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 0, 0, 1, ctypes.byref(_t(nv, 4, 0)), ws, 16, _stream()) == 0
+
+
+def test_rht_rejects_wide_mask(nv):
+    good = _t(nv, 4, 32)
+    st = nv.lib.rht16_quantize(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 1, 1 << 16, ctypes.byref(good),
+                               ctypes.c_void_p(FAKE), 16, _stream())
+    assert st == -1
+
+
+def test_gemm_rejects_bad_arguments(nv):
+    g = nv.lib.nvfp4_gemm
+    a, b = _t(nv, 8, 64), _t(nv, 16, 64)
+    c = ctypes.c_void_p(FAKE)
+    assert g(ctypes.byref(a), ctypes.byref(_t(nv, 16, 48)), c, 0, 16, 0, None, None, 0, _stream()) == -1  # K mismatch
+    assert g(ctypes.byref(a), ctypes.byref(b), c, 0, 8, 0, None, None, 0, _stream()) == -1  # ldc < N
+    assert g(ctypes.byref(a), ctypes.byref(b), c, 5, 16, 0, None, None, 0, _stream()) == -1  # dtype
+    assert g(ctypes.byref(a), ctypes.byref(b), c, 0, 16, 7, None, None, 0, _stream()) == -1  # epilogue
+    assert g(ctypes.byref(a), ctypes.byref(b), None, 0, 16, 0, None, None, 0, _stream()) == -1
+    assert g(ctypes.byref(a), ctypes.byref(b), c, 0, 16, 0, ctypes.c_void_p(FAKE + 2), None, 0, _stream()) == -1
+    assert g(ctypes.byref(_t(nv, 8, 40)), ctypes.byref(_t(nv, 16, 40)), c, 0, 16, 0, None, None, 0, _stream()) == -1
+    assert g(ctypes.byref(_t(nv, 0, 64)), ctypes.byref(b), c, 0, 16, 0, None, None, 0, _stream()) == 0
+
+
+def test_kv_rejects_bad_arguments(nv):
+    kq = nv.lib.nvfp4_kv_quant
+    out = _t(nv, 12 * 4 * 2, 32)
+    ws = ctypes.c_void_p(FAKE)
+    assert kq(ctypes.c_void_p(FAKE), 12, 4, 2, 32, 0, ctypes.byref(out), ws, 16, _stream()) == -1  # frame_block
+    assert kq(ctypes.c_void_p(FAKE), 12, 4, 2, 24, 8, ctypes.byref(_t(nv, 96, 24)), ws, 16, _stream()) == -1
+    assert kq(ctypes.c_void_p(FAKE), 12, 4, 2, 32, 8, ctypes.byref(_t(nv, 95, 32)), ws, 16, _stream()) == -1
+    assert kq(ctypes.c_void_p(FAKE), 40, 4, 2, 32, 8, ctypes.byref(_t(nv, 320, 32)), ws, 16, _stream()) == -3
+    kd = nv.lib.nvfp4_kv_dequant
+    assert kd(ctypes.byref(out), 12, 4, 2, 32, 8, None, _stream()) == -1
+    assert kd(ctypes.byref(out), 12, 4, 2, 32, 8, ctypes.c_void_p(FAKE + 8), _stream()) == -1
+    assert kd(ctypes.byref(_t(nv, 96, 16)), 12, 4, 2, 32, 8, ctypes.c_void_p(FAKE), _stream()) == -1
+
+
+def test_amax_encode_dequant_reject_bad_arguments(nv):
+    assert nv.lib.nvfp4_amax(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 0, None, _stream()) == -1
+    assert nv.lib.nvfp4_amax(ctypes.c_void_p(FAKE), 1, 4, 30, 32, 0, ctypes.c_void_p(FAKE), _stream()) == -1
+    assert nv.lib.nvfp4_amax(ctypes.c_void_p(FAKE), 1, 0, 32, 32, 0, ctypes.c_void_p(FAKE), _stream()) == 0
+    good = _t(nv, 64, 32)
+    enc = nv.lib.nvfp4_encode
+    assert enc(ctypes.c_void_p(FAKE), 1, 64, 32, 32, 1, 0, None, ctypes.byref(good), _stream()) == -1
+    assert enc(ctypes.c_void_p(FAKE), 1, 32, 64, 64, 0, 8, ctypes.c_void_p(FAKE), ctypes.byref(good), _stream()) == -1
+    assert enc(ctypes.c_void_p(FAKE), 1, 64, 32, 32, 1, -1, ctypes.c_void_p(FAKE), ctypes.byref(good), _stream()) == -1
+    dq = nv.lib.nvfp4_dequantize
+    assert dq(ctypes.byref(good), 0, None, 0, _stream()) == -1
+    assert dq(ctypes.byref(good), 0, ctypes.c_void_p(FAKE), 3, _stream()) == -1
+    assert dq(ctypes.byref(_t(nv, 0, 32)), 0, ctypes.c_void_p(FAKE), 0, _stream()) == 0
