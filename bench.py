@@ -88,7 +88,7 @@ def bench_attn_proj(nv, torch, wl, steps, warmup, nsets):
         sets.append({
             "x": x, "wq": wq,
             "xq": nv.NVFP4Tensor.empty(m, k, 1, "cuda"),
-            "ws": torch.empty(4, device="cuda"),
+            "ws": torch.empty(1024, device="cuda"),
             "y": torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
         })
     stream = torch.cuda.current_stream()
@@ -147,7 +147,7 @@ def bench_rows(nv, torch, wl, steps, warmup):
             s[nm] = _dev_bf16(torch, d[nm]).reshape(shape)
             s[nm + "q"] = nv.NVFP4Tensor.empty(12 * 880 * 24, 128, 2, "cuda")
             s[nm + "o"] = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
-        s["ws"] = torch.empty(8, device="cuda")
+        s["ws"] = torch.empty(2048, device="cuda")
         kvsets.append(s)
 
     def kvq(s, t):
@@ -177,7 +177,7 @@ def bench_rows(nv, torch, wl, steps, warmup):
     rsets = []
     for i in range(3):
         s = {"g": _dev_bf16(torch, d["g"]), "x": _dev_bf16(torch, d["x"]),
-             "gq": nv.NVFP4Tensor.empty(cols, rows, 1, "cuda"), "ws": torch.empty(4, device="cuda")}
+             "gq": nv.NVFP4Tensor.empty(cols, rows, 1, "cuda"), "ws": torch.empty(1024, device="cuda")}
         s["xq"] = nv.rht16_quantize(s["x"], d["mask"], axis=0)
         s["c"] = torch.empty((cols, cols), dtype=torch.float32, device="cuda")
         rsets.append(s)
@@ -207,7 +207,7 @@ def bench_rows(nv, torch, wl, steps, warmup):
     x = _dev_bf16(torch, d["x"])
     w1 = nv.quantize(torch.from_numpy(d["w1"]).cuda())
     w2 = nv.quantize(torch.from_numpy(d["w2"]).cuda())
-    bufs = {"xq": nv.NVFP4Tensor.empty(m, dm, 1, "cuda"), "ws": torch.empty(4, device="cuda"),
+    bufs = {"xq": nv.NVFP4Tensor.empty(m, dm, 1, "cuda"), "ws": torch.empty(1024, device="cuda"),
             "h": torch.empty((m, f), dtype=torch.float32, device="cuda"),
             "hmax": torch.empty(1, device="cuda"), "hq": nv.NVFP4Tensor.empty(m, f, 1, "cuda"),
             "y": torch.empty((m, dm), dtype=torch.bfloat16, device="cuda")}
@@ -245,7 +245,7 @@ def cpu_baseline(wl):
         oracle.gemm_ref(xq, wq, want_bound=False)
         reps += 1
         el = time.perf_counter() - t0
-        if el > 10.0 or reps >= 8:
+        if el > 10.0 or reps >= 40:
             break
     fl = 2.0 * rows * d["w"].shape[0] * d["w"].shape[1] * reps
     return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",

@@ -80,6 +80,7 @@ extern "C" {
 #define NVFP4_OP_RHT16    1
 #define NVFP4_OP_GEMM     2
 #define NVFP4_OP_KV_QUANT 3
+#define NVFP4_OP_AMAX     4
 
 /* An NVFP4 tensor (host struct holding device pointers), layout above. */
 typedef struct {
@@ -97,8 +98,11 @@ int nvfp4_version(void);
 const char *nvfp4_status_string(int status);
 
 /* Bytes of device workspace `op` needs for a rows x cols problem (for
- * NVFP4_OP_KV_QUANT: rows = frames, cols = frame_block).  The workspace
- * must be 16-byte aligned; its contents on entry do not matter. */
+ * NVFP4_OP_KV_QUANT: rows = frames, cols = frame_block; for NVFP4_OP_AMAX:
+ * cols = rows_per_domain).  The workspace holds the partial maxima of the
+ * amax pass (4 KiB per scaling domain); it must be 16-byte aligned and its
+ * contents on entry do not matter.  Calls that share a workspace must not
+ * overlap in time. */
 size_t nvfp4_workspace_bytes(int op, int64_t rows, int64_t cols);
 
 /*
@@ -106,10 +110,12 @@ size_t nvfp4_workspace_bytes(int op, int64_t rows, int64_t cols);
  * domain d, where domain d is rows [d*rows_per_domain, (d+1)*rows_per_domain)
  * (the last domain may be shorter; rows_per_domain = 0 means one domain).
  * x: device [rows][ld] of `dtype`.  amax: device float32
- * [ceil(rows/rows_per_domain)], overwritten.
+ * [ceil(rows/rows_per_domain)], overwritten.  The maximum is exact and does
+ * not depend on thread scheduling (partial maxima, no atomics).
+ * ws: >= nvfp4_workspace_bytes(NVFP4_OP_AMAX, rows, rows_per_domain).
  */
 int nvfp4_amax(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
-               int64_t rows_per_domain, float *amax, void *stream);
+               int64_t rows_per_domain, float *amax, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Encode (steps 2-6) given each domain's amax: writes codes, block scales
@@ -168,6 +174,20 @@ int rht16_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t
 int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype,
                int64_t ldc, int epilogue, float *amax_out, void *ws, size_t ws_bytes,
                void *stream);
+
+/*
+ * nvfp4_gemm with an explicit tile shape instead of the built-in choice.
+ * tile_fa x tile_fb is the number of 32x32 MFMA fragments per wavefront
+ * along M x N (a workgroup covers 64*tile_fa x 64*tile_fb outputs); the
+ * supported shapes are 2x4, 4x2, 3x3 and 4x4, used when K % 128 == 0 (other
+ * K always take the bounds-checked 2x4 kernel).  Results are identical in
+ * tolerance, not bit-for-bit, across shapes (the fp32 summation order of an
+ * output element is the same; only scheduling differs).  Unsupported shapes
+ * return NVFP4_EINVAL.  Intended for tuning and testing.
+ */
+int nvfp4_gemm_tiled(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype,
+                     int64_t ldc, int epilogue, float *amax_out, int tile_fa, int tile_fb,
+                     void *stream);
 
 /*
  * KV-cache quantization in frame blocks (hyper.ai summary of the LongLive-2.0

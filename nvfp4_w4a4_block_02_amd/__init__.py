@@ -5,8 +5,10 @@ with torch (device memory is torch's), passes raw device pointers and the
 current HIP stream to the C ABI declared in ``include/nvfp4.h``, and turns a
 non-zero status into an exception.  All arithmetic runs in the HIP kernels.
 
-The library must have been built (``python -m nvfp4_w4a4_block_02_amd.build``);
-importing this module raises if it is missing — there is no fallback path.
+The library must have been built (``python -m nvfp4_w4a4_block_02_amd.build``).
+It is loaded on first use (so that the build module itself can be imported
+before it exists); every entry point raises if it is missing — there is no
+fallback path.
 """
 
 from __future__ import annotations
@@ -22,7 +24,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "libnvfp4.so")
 
 F32, BF16 = 0, 1
 EPI_NONE, EPI_GELU_TANH = 0, 1
-OP_QUANTIZE, OP_RHT16, OP_GEMM, OP_KV_QUANT = 0, 1, 2, 3
+OP_QUANTIZE, OP_RHT16, OP_GEMM, OP_KV_QUANT, OP_AMAX = 0, 1, 2, 3, 4
 
 
 class NVFP4Error(RuntimeError):
@@ -51,11 +53,12 @@ def _load():
         "nvfp4_version": (I, []),
         "nvfp4_status_string": (ctypes.c_char_p, [I]),
         "nvfp4_workspace_bytes": (SZ, [I, I64, I64]),
-        "nvfp4_amax": (I, [P, I, I64, I64, I64, I64, P, P]),
+        "nvfp4_amax": (I, [P, I, I64, I64, I64, I64, P, P, SZ, P]),
         "nvfp4_encode": (I, [P, I, I64, I64, I64, I, I64, P, TP, P]),
         "nvfp4_quantize": (I, [P, I, I64, I64, I64, I, TP, P, SZ, P]),
         "rht16_quantize": (I, [P, I, I64, I64, I64, I, U32, TP, P, SZ, P]),
         "nvfp4_gemm": (I, [TP, TP, P, I, I64, I, P, P, SZ, P]),
+        "nvfp4_gemm_tiled": (I, [TP, TP, P, I, I64, I, P, I, I, P]),
         "nvfp4_kv_quant": (I, [P, I64, I64, I64, I64, I64, TP, P, SZ, P]),
         "nvfp4_kv_dequant": (I, [TP, I64, I64, I64, I64, I64, P, P]),
         "nvfp4_dequantize": (I, [TP, I64, P, I, P]),
@@ -67,15 +70,30 @@ def _load():
     return lib
 
 
-lib = _load()
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def __getattr__(name):  # module attribute `lib` loads the library on first access
+    if name == "lib":
+        return _lib()
+    raise AttributeError(name)
+
+
 EXPORTED = ("nvfp4_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_amax",
-            "nvfp4_encode", "nvfp4_quantize", "rht16_quantize", "nvfp4_gemm", "nvfp4_kv_quant",
+            "nvfp4_encode", "nvfp4_quantize", "rht16_quantize", "nvfp4_gemm", "nvfp4_gemm_tiled", "nvfp4_kv_quant",
             "nvfp4_kv_dequant", "nvfp4_dequantize")
 
 
 def _check(status: int, what: str):
     if status != 0:
-        raise NVFP4Error(f"{what}: {lib.nvfp4_status_string(status).decode()} ({status})")
+        raise NVFP4Error(f"{what}: {_lib().nvfp4_status_string(status).decode()} ({status})")
 
 
 def _stream(stream=None):
@@ -126,7 +144,7 @@ class NVFP4Tensor:
 
 
 def workspace_bytes(op: int, rows: int, cols: int) -> int:
-    return int(lib.nvfp4_workspace_bytes(op, rows, cols))
+    return int(_lib().nvfp4_workspace_bytes(op, rows, cols))
 
 
 def _workspace(op, rows, cols, device):
@@ -149,13 +167,16 @@ def _out_shape(x: torch.Tensor, axis: int):
     return (rows, cols) if axis == 1 else (cols, rows)
 
 
-def amax(x: torch.Tensor, rows_per_domain: int = 0, out: torch.Tensor | None = None, stream=None):
+def amax(x: torch.Tensor, rows_per_domain: int = 0, out: torch.Tensor | None = None,
+         ws: torch.Tensor | None = None, stream=None):
     rows, cols = x.shape
     nd = 1 if rows_per_domain <= 0 or rows_per_domain >= rows else -(-rows // rows_per_domain)
     if out is None:
         out = torch.empty((nd,), dtype=torch.float32, device=x.device)
-    _check(lib.nvfp4_amax(_ptr(x), _dtype_code(x), rows, cols, _ld(x), rows_per_domain, _ptr(out),
-                          _stream(stream)), "nvfp4_amax")
+    if ws is None:
+        ws = _workspace(OP_AMAX, rows, rows_per_domain, x.device)
+    _check(_lib().nvfp4_amax(_ptr(x), _dtype_code(x), rows, cols, _ld(x), rows_per_domain, _ptr(out),
+                          _ptr(ws), ws.numel() * 4, _stream(stream)), "nvfp4_amax")
     return out
 
 
@@ -166,7 +187,7 @@ def encode(x: torch.Tensor, amax_t: torch.Tensor, axis: int = 1, rows_per_domain
         r, k = _out_shape(x, axis)
         out = NVFP4Tensor.empty(r, k, amax_t.numel(), x.device)
     ct = out.c()
-    _check(lib.nvfp4_encode(_ptr(x), _dtype_code(x), rows, cols, _ld(x), axis, rows_per_domain,
+    _check(_lib().nvfp4_encode(_ptr(x), _dtype_code(x), rows, cols, _ld(x), axis, rows_per_domain,
                             _ptr(amax_t), ctypes.byref(ct), _stream(stream)), "nvfp4_encode")
     return out
 
@@ -180,7 +201,7 @@ def quantize(x: torch.Tensor, axis: int = 1, out: NVFP4Tensor | None = None, ws:
     if ws is None:
         ws = _workspace(OP_QUANTIZE, rows, cols, x.device)
     ct = out.c()
-    _check(lib.nvfp4_quantize(_ptr(x), _dtype_code(x), rows, cols, _ld(x), axis, ctypes.byref(ct),
+    _check(_lib().nvfp4_quantize(_ptr(x), _dtype_code(x), rows, cols, _ld(x), axis, ctypes.byref(ct),
                               _ptr(ws), ws.numel() * 4, _stream(stream)), "nvfp4_quantize")
     return out
 
@@ -194,18 +215,26 @@ def rht16_quantize(x: torch.Tensor, sign_mask: int, axis: int = 1, out: NVFP4Ten
     if ws is None:
         ws = _workspace(OP_RHT16, rows, cols, x.device)
     ct = out.c()
-    _check(lib.rht16_quantize(_ptr(x), _dtype_code(x), rows, cols, _ld(x), axis, sign_mask,
+    _check(_lib().rht16_quantize(_ptr(x), _dtype_code(x), rows, cols, _ld(x), axis, sign_mask,
                               ctypes.byref(ct), _ptr(ws), ws.numel() * 4, _stream(stream)), "rht16_quantize")
     return out
 
 
 def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.bfloat16, epilogue: int = EPI_NONE,
-         amax_out: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+         amax_out: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None,
+         tiles: tuple[int, int] | None = None) -> torch.Tensor:
+    """C = A @ B^T on NVFP4 operands (B is [N, K]).  ``tiles`` pins the
+    (fragments along M, fragments along N) per wavefront; default: automatic."""
     if out is None:
         out = torch.empty((a.rows, b.rows), dtype=out_dtype, device=a.codes.device)
     ca, cb = a.c(), b.c()
-    _check(lib.nvfp4_gemm(ctypes.byref(ca), ctypes.byref(cb), _ptr(out), _dtype_code(out), _ld(out),
-                          epilogue, _ptr(amax_out), None, 0, _stream(stream)), "nvfp4_gemm")
+    if tiles is None:
+        _check(_lib().nvfp4_gemm(ctypes.byref(ca), ctypes.byref(cb), _ptr(out), _dtype_code(out), _ld(out),
+                              epilogue, _ptr(amax_out), None, 0, _stream(stream)), "nvfp4_gemm")
+    else:
+        _check(_lib().nvfp4_gemm_tiled(ctypes.byref(ca), ctypes.byref(cb), _ptr(out), _dtype_code(out), _ld(out),
+                                    epilogue, _ptr(amax_out), tiles[0], tiles[1], _stream(stream)),
+               "nvfp4_gemm_tiled")
     return out
 
 
@@ -220,7 +249,7 @@ def kv_quant(kv: torch.Tensor, frame_block: int = 8, out: NVFP4Tensor | None = N
     if ws is None:
         ws = _workspace(OP_KV_QUANT, f, frame_block, kv.device)
     ct = out.c()
-    _check(lib.nvfp4_kv_quant(_ptr(kv), f, t, h, d, frame_block, ctypes.byref(ct), _ptr(ws), ws.numel() * 4,
+    _check(_lib().nvfp4_kv_quant(_ptr(kv), f, t, h, d, frame_block, ctypes.byref(ct), _ptr(ws), ws.numel() * 4,
                               _stream(stream)), "nvfp4_kv_quant")
     return out
 
@@ -231,7 +260,7 @@ def kv_dequant(q: NVFP4Tensor, shape, frame_block: int = 8, out: torch.Tensor | 
     if out is None:
         out = torch.empty((f, t, h, d), dtype=torch.bfloat16, device=q.codes.device)
     ct = q.c()
-    _check(lib.nvfp4_kv_dequant(ctypes.byref(ct), f, t, h, d, frame_block, _ptr(out), _stream(stream)),
+    _check(_lib().nvfp4_kv_dequant(ctypes.byref(ct), f, t, h, d, frame_block, _ptr(out), _stream(stream)),
            "nvfp4_kv_dequant")
     return out
 
@@ -241,7 +270,7 @@ def dequantize(q: NVFP4Tensor, dtype=torch.float32, rows_per_domain: int = 0, ou
     if out is None:
         out = torch.empty((q.rows, q.k), dtype=dtype, device=q.codes.device)
     ct = q.c()
-    _check(lib.nvfp4_dequantize(ctypes.byref(ct), rows_per_domain, _ptr(out), _dtype_code(out), _stream(stream)),
+    _check(_lib().nvfp4_dequantize(ctypes.byref(ct), rows_per_domain, _ptr(out), _dtype_code(out), _stream(stream)),
            "nvfp4_dequantize")
     return out
 

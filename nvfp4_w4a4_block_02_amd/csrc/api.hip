@@ -70,31 +70,39 @@ const char* nvfp4_status_string(int status) {
 }
 
 size_t nvfp4_workspace_bytes(int op, int64_t rows, int64_t cols) {
+  // The amax passes keep at most kMaxParts partial maxima per scaling domain.
+  const int64_t per_domain = (int64_t)nvfp4::kMaxParts * 4;
   switch (op) {
     case NVFP4_OP_QUANTIZE:
     case NVFP4_OP_RHT16:
-      return 16;  // one float32 amax, padded to the alignment
+    case NVFP4_OP_AMAX:
+      return (size_t)per_domain * (op == NVFP4_OP_AMAX ? (size_t)ndomains(rows, cols) : 1u);
     case NVFP4_OP_GEMM:
       return 0;
-    case NVFP4_OP_KV_QUANT: {
-      const int64_t nd = ndomains(rows, cols);
-      return (size_t)((nd * 4 + 15) / 16 * 16);
-    }
+    case NVFP4_OP_KV_QUANT:
+      return (size_t)(ndomains(rows, cols) * per_domain);
     default:
       return 0;
   }
 }
 
 int nvfp4_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
-               int64_t rows_per_domain, float* amax, void* stream) {
+               int64_t rows_per_domain, float* amax, void* ws, size_t ws_bytes, void* stream) {
   if (!x || !amax || !valid_dtype(dtype) || rows < 0 || cols < 0 || cols % 16 != 0 || ld < cols ||
       !aligned16(x) || !ld_ok(ld, dtype) || rows_per_domain < 0)
     return NVFP4_EINVAL;
+  if (!ws || !aligned16(ws)) return NVFP4_EINVAL;
+  if (ws_bytes < nvfp4_workspace_bytes(NVFP4_OP_AMAX, rows, rows_per_domain)) return NVFP4_EWORKSPACE;
   if (rows * (cols / 16) >= kMaxBlocks) return NVFP4_EUNSUPPORTED;
   if (rows == 0) return NVFP4_OK;
-  if (cols == 0) return from_hip(nvfp4::launch_zero(amax, ndomains(rows, rows_per_domain), (hipStream_t)stream));
-  return from_hip(nvfp4::launch_amax_rows(x, dtype, rows, cols, ld, rows_per_domain, amax, false, 0,
-                                          (hipStream_t)stream));
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t nd = ndomains(rows, rows_per_domain);
+  if (cols == 0) return from_hip(nvfp4::launch_zero(amax, nd, s));
+  float* parts = static_cast<float*>(ws);
+  const uint32_t np = nvfp4::amax_parts_rows(rows, cols, rows_per_domain);
+  if (nvfp4::launch_amax_parts_rows(x, dtype, rows, cols, ld, rows_per_domain, parts, np, false, 0, s) != hipSuccess)
+    return NVFP4_EHIP;
+  return from_hip(nvfp4::launch_reduce_parts(parts, np, nd, amax, s));
 }
 
 int nvfp4_encode(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int axis,
@@ -106,8 +114,9 @@ int nvfp4_encode(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
   if (rows == 0 || cols == 0) return NVFP4_OK;
   hipStream_t s = (hipStream_t)stream;
   if (axis == 1)
-    return from_hip(nvfp4::launch_encode_rows(x, dtype, rows, cols, ld, rows_per_domain, amax, qout(out), false, 0, s));
-  return from_hip(nvfp4::launch_encode_cols(x, dtype, rows, cols, ld, amax, qout(out), false, 0, s));
+    return from_hip(nvfp4::launch_encode_rows(x, dtype, rows, cols, ld, rows_per_domain, amax, 1, qout(out),
+                                              false, 0, s));
+  return from_hip(nvfp4::launch_encode_cols(x, dtype, rows, cols, ld, amax, 1, qout(out), false, 0, s));
 }
 
 static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int axis,
@@ -120,17 +129,20 @@ static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, i
   if (ws_bytes < nvfp4_workspace_bytes(NVFP4_OP_QUANTIZE, rows, cols)) return NVFP4_EWORKSPACE;
   if (rows == 0 || cols == 0) return NVFP4_OK;
   hipStream_t s = (hipStream_t)stream;
-  float* amax = static_cast<float*>(ws);
+  float* parts = static_cast<float*>(ws);
   hipError_t e;
+  uint32_t np;
   if (axis == 1 || !rht) {
     // Without the transform the amax does not depend on the block direction.
-    e = nvfp4::launch_amax_rows(x, dtype, rows, cols, ld, 0, amax, rht && axis == 1, mask, s);
+    np = nvfp4::amax_parts_rows(rows, cols, 0);
+    e = nvfp4::launch_amax_parts_rows(x, dtype, rows, cols, ld, 0, parts, np, rht, mask, s);
   } else {
-    e = nvfp4::launch_amax_cols_rht(x, dtype, rows, cols, ld, amax, mask, s);
+    np = nvfp4::amax_parts_cols(rows, cols);
+    e = nvfp4::launch_amax_parts_cols(x, dtype, rows, cols, ld, parts, np, rht, mask, s);
   }
   if (e != hipSuccess) return NVFP4_EHIP;
-  if (axis == 1) e = nvfp4::launch_encode_rows(x, dtype, rows, cols, ld, 0, amax, qout(out), rht, mask, s);
-  else e = nvfp4::launch_encode_cols(x, dtype, rows, cols, ld, amax, qout(out), rht, mask, s);
+  if (axis == 1) e = nvfp4::launch_encode_rows(x, dtype, rows, cols, ld, 0, parts, np, qout(out), rht, mask, s);
+  else e = nvfp4::launch_encode_cols(x, dtype, rows, cols, ld, parts, np, qout(out), rht, mask, s);
   return from_hip(e);
 }
 
@@ -144,10 +156,8 @@ int rht16_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t
   return quantize_impl(x, dtype, rows, cols, ld, axis, true, sign_mask, out, ws, ws_bytes, stream);
 }
 
-int nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int c_dtype, int64_t ldc,
-               int epilogue, float* amax_out, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
+static int gemm_impl(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int c_dtype, int64_t ldc,
+                     int epilogue, float* amax_out, int tile_fa, int tile_fb, void* stream) {
   if (!tensor_ok(a) || !tensor_ok(b) || !c || !valid_dtype(c_dtype)) return NVFP4_EINVAL;
   if (a->k != b->k || ldc < b->rows || !aligned16(c)) return NVFP4_EINVAL;
   if (epilogue != NVFP4_EPI_NONE && epilogue != NVFP4_EPI_GELU_TANH) return NVFP4_EINVAL;
@@ -159,7 +169,20 @@ int nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int c_dtyp
     return amax_out ? from_hip(nvfp4::launch_zero(amax_out, 1, s)) : NVFP4_OK;
   }
   return from_hip(nvfp4::launch_gemm(qout(a), qout(b), a->rows, b->rows, a->k, c, c_dtype, ldc, epilogue,
-                                     amax_out, s));
+                                     amax_out, tile_fa, tile_fb, s));
+}
+
+int nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int c_dtype, int64_t ldc,
+               int epilogue, float* amax_out, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return gemm_impl(a, b, c, c_dtype, ldc, epilogue, amax_out, 0, 0, stream);
+}
+
+int nvfp4_gemm_tiled(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int c_dtype, int64_t ldc,
+                     int epilogue, float* amax_out, int tile_fa, int tile_fb, void* stream) {
+  if (!nvfp4::gemm_tiles_supported(tile_fa, tile_fb)) return NVFP4_EINVAL;
+  return gemm_impl(a, b, c, c_dtype, ldc, epilogue, amax_out, tile_fa, tile_fb, stream);
 }
 
 int nvfp4_kv_quant(const void* kv, int64_t frames, int64_t tokens, int64_t heads, int64_t head_dim,
@@ -175,11 +198,13 @@ int nvfp4_kv_quant(const void* kv, int64_t frames, int64_t tokens, int64_t heads
   if (rows == 0 || head_dim == 0) return NVFP4_OK;
   hipStream_t s = (hipStream_t)stream;
   const int64_t rpd = frame_block * tokens * heads;
-  float* amax = static_cast<float*>(ws);
-  hipError_t e = nvfp4::launch_amax_rows(kv, NVFP4_BF16, rows, head_dim, head_dim, rpd, amax, false, 0, s);
-  if (e != hipSuccess) return NVFP4_EHIP;
-  return from_hip(nvfp4::launch_encode_rows(kv, NVFP4_BF16, rows, head_dim, head_dim, rpd, amax, qout(out),
-                                            false, 0, s));
+  float* parts = static_cast<float*>(ws);
+  const uint32_t np = nvfp4::amax_parts_rows(rows, head_dim, rpd);
+  if (nvfp4::launch_amax_parts_rows(kv, NVFP4_BF16, rows, head_dim, head_dim, rpd, parts, np, false, 0, s) !=
+      hipSuccess)
+    return NVFP4_EHIP;
+  return from_hip(nvfp4::launch_encode_rows(kv, NVFP4_BF16, rows, head_dim, head_dim, rpd, parts, np,
+                                            qout(out), false, 0, s));
 }
 
 int nvfp4_kv_dequant(const nvfp4_tensor* in, int64_t frames, int64_t tokens, int64_t heads, int64_t head_dim,

@@ -15,22 +15,35 @@
 // block scale — and fed to v_mfma_f32_32x32x16_f16, which accumulates the
 // exact products in float32.  The tensor scales are applied in the epilogue.
 //
-// Work split.  A workgroup of 4 wavefronts computes a (2*WM) x (2*WN) tile;
-// each wavefront a WM x WN sub-tile made of FA x FB 32x32 MFMA fragments.
-// K advances 128 elements (8 NVFP4 blocks, 64 bytes of codes per row) at a
-// time.  Within a K-tile, lanes 0-31 own k in [0, 64) and lanes 32-63 own
-// k in [64, 128) of their row (A) or column (B): a lane loads its 32 code
-// bytes and 4 scale bytes with two 16-byte and one 4-byte load per fragment,
-// and MFMA step s (0..7) consumes code dword s.  The MFMA reduction runs over
-// any k as long as A and B use the same assignment, which they do.
+// Work split.  A workgroup of 4 wavefronts (2 x 2) computes a
+// (64 FA) x (64 FB) tile; each wavefront a (32 FA) x (32 FB) sub-tile made of
+// FA x FB 32x32 MFMA fragments.  K advances 128 elements (8 NVFP4 blocks, 64
+// code bytes per row) per tile.  Within a K-tile, lanes 0-31 own k in
+// [0, 64) and lanes 32-63 own k in [64, 128) of their row (A) or column (B);
+// MFMA step s (0..7) consumes code dword s of the lane, so each step covers
+// k = {8s..8s+7} and {64+8s..64+8s+7}.  The MFMA reduction runs over any k as
+// long as A and B use the same assignment, which they do.
+//
+// Main kernel (K a multiple of 128): a 3-stage LDS ring fed by direct
+// global->LDS loads (global_load_lds_dwordx4 / _dword).  Every K-tile is read
+// from memory once per workgroup; its LDS image is laid out in the order the
+// consuming lanes read it (fragment, 16-byte half, lane), so the ds_reads are
+// contiguous and conflict-free.  One barrier per K-tile; loads run two tiles
+// ahead.  Decode of step s+1 is interleaved with the MFMAs of step s.
+//
+// Fallback kernel (any K % 16 == 0): the same fragments loaded straight into
+// registers with bounds checks; code bytes past K read as 0.
 #include "device.h"
 #include "internal.h"
 
 namespace nvfp4 {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kKT = 128;  // K elements per main-loop iteration
+typedef __attribute__((address_space(1))) const void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
+constexpr int kKT = 128;    // K elements per tile
+constexpr int kStages = 3;  // LDS ring depth
 
 __device__ __forceinline__ half8_t decode8(uint32_t codes, half2_t sig2) {
   half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * sig2;
@@ -43,15 +56,13 @@ __device__ __forceinline__ half8_t decode8(uint32_t codes, half2_t sig2) {
   return r;
 }
 
-// Four E4M3 bytes -> four fp16 broadcast pairs (exact: every E4M3 value is an
-// fp16 value).
-__device__ __forceinline__ void scales_to_h2(uint32_t sw, half2_t (&s2)[4]) {
+// Byte q (0..3) of four E4M3 scale bytes as an fp16 broadcast pair (exact:
+// every E4M3 value is an fp16 value).
+__device__ __forceinline__ half2_t scale_h2(uint32_t sw, int q) {
   const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
   const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true);
-  s2[0] = half2_t{lo.x, lo.x};
-  s2[1] = half2_t{lo.y, lo.y};
-  s2[2] = half2_t{hi.x, hi.x};
-  s2[3] = half2_t{hi.y, hi.y};
+  const _Float16 v = q == 0 ? lo.x : q == 1 ? lo.y : q == 2 ? hi.x : hi.y;
+  return half2_t{v, v};
 }
 
 __device__ __forceinline__ float gelu_tanh(float h) {
@@ -59,169 +70,65 @@ __device__ __forceinline__ float gelu_tanh(float h) {
   return 0.5f * h * (1.0f + tanhf(c * (h + 0.044715f * h * h * h)));
 }
 
+// One K-tile of this lane's fragments: 32 code bytes and 4 scale bytes each.
 template <int FA, int FB>
-struct Tile {
-  uint4 a[FA][2];
-  uint4 b[FB][2];
+struct Frags {
+  u32x4_t a[FA][2];
+  u32x4_t b[FB][2];
   uint32_t sa[FA];
   uint32_t sb[FB];
 };
 
 template <int FA, int FB>
-__device__ __forceinline__ void load_tile_fast(Tile<FA, FB>& t, const uint8_t* const (&pa)[FA],
-                                               const uint8_t* const (&psa)[FA],
-                                               const uint8_t* const (&pb)[FB],
-                                               const uint8_t* const (&psb)[FB], int kt) {
+__device__ __forceinline__ void decode_step(const Frags<FA, FB>& t, int s, half8_t (&A)[FA], half8_t (&B)[FB]) {
 #pragma unroll
-  for (int f = 0; f < FA; ++f) {
-    const uint4* p = reinterpret_cast<const uint4*>(pa[f] + kt / 2);
-    t.a[f][0] = p[0];
-    t.a[f][1] = p[1];
-    t.sa[f] = *reinterpret_cast<const uint32_t*>(psa[f] + kt / 16);
-  }
+  for (int f = 0; f < FA; ++f) A[f] = decode8(t.a[f][s >> 2][s & 3], scale_h2(t.sa[f], s >> 1));
 #pragma unroll
-  for (int f = 0; f < FB; ++f) {
-    const uint4* p = reinterpret_cast<const uint4*>(pb[f] + kt / 2);
-    t.b[f][0] = p[0];
-    t.b[f][1] = p[1];
-    t.sb[f] = *reinterpret_cast<const uint32_t*>(psb[f] + kt / 16);
-  }
-}
-
-// Generic K: any K % 16 == 0.  Code dwords and scale bytes past K read as 0
-// (decoding to +0), so the partial last K-tile needs no other special case.
-template <int FA, int FB>
-__device__ __forceinline__ void load_tile_checked(Tile<FA, FB>& t, const uint8_t* const (&pa)[FA],
-                                                  const uint8_t* const (&psa)[FA],
-                                                  const uint8_t* const (&pb)[FB],
-                                                  const uint8_t* const (&psb)[FB], int kt, int K,
-                                                  int hh) {
-  // `row` arguments already point at this lane's first code byte / scale byte
-  // of the tile (k = kt + 64 * hh).
-  const int kl = kt + 64 * hh;
-  auto ld_codes = [&](const uint8_t* row, uint4 (&dst)[2]) {
-    uint32_t w[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int k0 = kl + 8 * s;
-      w[s] = (k0 < K) ? *reinterpret_cast<const uint32_t*>(row + 4 * s) : 0u;
-    }
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  };
-  auto ld_scales = [&](const uint8_t* row) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k0 = kl + 16 * q;
-      if (k0 < K) v |= (uint32_t)row[q] << (8 * q);
-    }
-    return v;
-  };
-#pragma unroll
-  for (int f = 0; f < FA; ++f) {
-    ld_codes(pa[f] + kt / 2, t.a[f]);
-    t.sa[f] = ld_scales(psa[f] + kt / 16);
-  }
-#pragma unroll
-  for (int f = 0; f < FB; ++f) {
-    ld_codes(pb[f] + kt / 2, t.b[f]);
-    t.sb[f] = ld_scales(psb[f] + kt / 16);
-  }
-}
-
-__device__ __forceinline__ uint32_t dword_of(const uint4 (&c)[2], int s) {
-  const uint4 q = c[s >> 2];
-  switch (s & 3) {
-    case 0: return q.x;
-    case 1: return q.y;
-    case 2: return q.z;
-    default: return q.w;
-  }
+  for (int f = 0; f < FB; ++f) B[f] = decode8(t.b[f][s >> 2][s & 3], scale_h2(t.sb[f], s >> 1));
 }
 
 template <int FA, int FB>
-__device__ __forceinline__ void compute_tile(const Tile<FA, FB>& t, float16_t (&acc)[FA][FB]) {
-  half2_t sa2[FA][4], sb2[FB][4];
-#pragma unroll
-  for (int f = 0; f < FA; ++f) scales_to_h2(t.sa[f], sa2[f]);
-#pragma unroll
-  for (int f = 0; f < FB; ++f) scales_to_h2(t.sb[f], sb2[f]);
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    half8_t av[FA], bv[FB];
-#pragma unroll
-    for (int f = 0; f < FA; ++f) av[f] = decode8(dword_of(t.a[f], s), sa2[f][s >> 1]);
-#pragma unroll
-    for (int f = 0; f < FB; ++f) bv[f] = decode8(dword_of(t.b[f], s), sb2[f][s >> 1]);
-#pragma unroll
-    for (int i = 0; i < FA; ++i)
-#pragma unroll
-      for (int j = 0; j < FB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
-  }
-}
-
-template <int FA, int FB, int OUT, int EPI, bool FAST>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(
-    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
-    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts,
-    void* __restrict__ c, int64_t ldc, int M, int N, int K, float* __restrict__ amax_out) {
-  constexpr int WM = 32 * FA, WN = 32 * FB;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int li = lane & 31, hh = lane >> 5;
-  const int m0 = blockIdx.y * (2 * WM) + (wave >> 1) * WM;
-  const int n0 = blockIdx.x * (2 * WN) + (wave & 1) * WN;
-  const int64_t cpitch = K / 2, spitch = K / 16;
-
-  const uint8_t* pa[FA];
-  const uint8_t* psa[FA];
-  const uint8_t* pb[FB];
-  const uint8_t* psb[FB];
-#pragma unroll
-  for (int f = 0; f < FA; ++f) {
-    const int row = min(m0 + 32 * f + li, M - 1);  // clamp: rows past M are computed, never stored
-    pa[f] = ac + (int64_t)row * cpitch + 32 * hh;
-    psa[f] = as + (int64_t)row * spitch + 4 * hh;
-  }
-#pragma unroll
-  for (int f = 0; f < FB; ++f) {
-    const int col = min(n0 + 32 * f + li, N - 1);
-    pb[f] = bc + (int64_t)col * cpitch + 32 * hh;
-    psb[f] = bs + (int64_t)col * spitch + 4 * hh;
-  }
-
-  float16_t acc[FA][FB];
+__device__ __forceinline__ void mfma_step(const half8_t (&A)[FA], const half8_t (&B)[FB], float16_t (&acc)[FA][FB]) {
 #pragma unroll
   for (int i = 0; i < FA; ++i)
 #pragma unroll
-    for (int j = 0; j < FB; ++j)
+    for (int j = 0; j < FB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[j], acc[i][j], 0, 0, 0);
+}
+
+// Ask the scheduler to alternate one MFMA with the decode VALU work of the
+// next step.
+template <int FA, int FB>
+__device__ __forceinline__ void interleave_hint() {
+  constexpr int nv = (8 * (FA + FB) + FA * FB - 1) / (FA * FB);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  if constexpr (FAST) {
-    // Ping-pong between two register tiles so the loads of the next K-tile
-    // are in flight while the current one is decoded and multiplied.
-    Tile<FA, FB> t0, t1;
-    load_tile_fast(t0, pa, psa, pb, psb, 0);
-    int kt = 0;
-    for (; kt + 2 * kKT <= K; kt += 2 * kKT) {
-      load_tile_fast(t1, pa, psa, pb, psb, kt + kKT);
-      compute_tile(t0, acc);
-      if (kt + 2 * kKT < K) load_tile_fast(t0, pa, psa, pb, psb, kt + 2 * kKT);
-      compute_tile(t1, acc);
-    }
-    if (kt < K) compute_tile(t0, acc);  // odd number of K-tiles
-  } else {
-    Tile<FA, FB> cur;
-    for (int kt = 0; kt < K; kt += kKT) {
-      load_tile_checked(cur, pa, psa, pb, psb, kt, K, hh);
-      compute_tile(cur, acc);
-    }
+  for (int i = 0; i < FA * FB; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, nv, 0);
   }
+}
 
-  // Epilogue: tensor scales, optional GELU, store, optional amax.
-  const float sab = ats[0] * bts[0];
+// All 8 MFMA steps of one K-tile; the decode of step s+1 overlaps step s.
+template <int FA, int FB>
+__device__ __forceinline__ void compute_tile(const Frags<FA, FB>& t, float16_t (&acc)[FA][FB]) {
+  half8_t A0[FA], B0[FB], A1[FA], B1[FB];
+  decode_step(t, 0, A0, B0);
+#pragma unroll
+  for (int s = 0; s < 8; s += 2) {
+    mfma_step(A0, B0, acc);
+    decode_step(t, s + 1, A1, B1);
+    interleave_hint<FA, FB>();
+    mfma_step(A1, B1, acc);
+    if (s + 2 < 8) decode_step(t, s + 2, A0, B0);
+    interleave_hint<FA, FB>();
+  }
+}
+
+// Epilogue: tensor scales, optional GELU, store, optional amax of the stored
+// values.  MFMA 32x32 output layout: lane l, accumulator r holds row
+// (r / 4) * 8 + (l / 32) * 4 + r % 4, column l % 32 of the fragment.
+template <int FA, int FB, int OUT, int EPI>
+__device__ __forceinline__ void store_tile(const float16_t (&acc)[FA][FB], float sab, int m0, int n0, int li, int hh,
+                                           int M, int N, void* __restrict__ c, int64_t ldc, float* __restrict__ amax_out) {
   float mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < FA; ++i) {
@@ -248,41 +155,270 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   }
   if (amax_out != nullptr) {
     mx = wave_max(mx);
-    if (lane == 0 && mx > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(amax_out), __float_as_uint(mx));
+    if ((threadIdx.x & 63) == 0 && mx > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(amax_out), __float_as_uint(mx));
   }
 }
 
-template <int FA, int FB>
-hipError_t launch_tiles(QOut a, QOut b, int m, int n, int k, void* c, int c_dt, int64_t ldc,
-                        int epi, float* amax_out, bool fast, hipStream_t s) {
-  const dim3 grid((unsigned)((n + 64 * FB - 1) / (64 * FB)), (unsigned)((m + 64 * FA - 1) / (64 * FA)));
-#define NVFP4_GEMM_LAUNCH(OUT, EPI, FASTV)                                                  \
-  gemm_kernel<FA, FB, OUT, EPI, FASTV><<<grid, kThreads, 0, s>>>(                           \
-      a.codes, a.scales, a.tscale, b.codes, b.scales, b.tscale, c, ldc, m, n, k, amax_out)
-#define NVFP4_GEMM_EPI(OUT, FASTV)                 \
-  if (epi == 1) NVFP4_GEMM_LAUNCH(OUT, 1, FASTV); \
-  else NVFP4_GEMM_LAUNCH(OUT, 0, FASTV);
-  if (fast) {
-    if (c_dt == 0) { NVFP4_GEMM_EPI(0, true) } else { NVFP4_GEMM_EPI(1, true) }
-  } else {
-    if (c_dt == 0) { NVFP4_GEMM_EPI(0, false) } else { NVFP4_GEMM_EPI(1, false) }
+// Workgroup -> output tile.  Workgroups are dealt round-robin to the 8 XCDs
+// (each with its own L2); renumber so that XCD x works on a contiguous range
+// of tiles in row-major order, which keeps the A rows and B columns an XCD
+// touches together.
+__device__ __forceinline__ void tile_of(int tiles_n, int ntiles, int& tm, int& tn) {
+  const int id = blockIdx.x;
+  int t = id;
+  if (ntiles % 8 == 0) t = (id % 8) * (ntiles / 8) + id / 8;
+  tm = t / tiles_n;
+  tn = t - tm * tiles_n;
+}
+
+// ---------------------------------------------------------------------------
+// Main kernel: K % 128 == 0.
+template <int FA, int FB, int OUT, int EPI>
+__global__ __launch_bounds__(256) void gemm_lds_kernel(
+    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
+    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts,
+    void* __restrict__ c, int64_t ldc, int M, int N, int K, float* __restrict__ amax_out) {
+  constexpr int NFA = 2 * FA, NFB = 2 * FB;                  // fragments per workgroup
+  constexpr int OFF_B = NFA * 2048, OFF_SA = OFF_B + NFB * 2048, OFF_SB = OFF_SA + NFA * 256;
+  constexpr int STAGE = OFF_SB + NFB * 256;
+  static_assert((FA + FB) % 2 == 0, "load slots assume FA + FB even");
+  constexpr int CPW = FA + FB;        // 16-byte code loads per wave per tile
+  constexpr int SPW = (FA + FB) / 2;  // 4-byte scale loads per wave per tile
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * STAGE];
+
+  const int l = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = l & 31, hh = l >> 5;
+  const int tiles_n = (N + 64 * FB - 1) / (64 * FB);
+  const int tiles_m = (M + 64 * FA - 1) / (64 * FA);
+  int tm, tn;
+  tile_of(tiles_n, tiles_m * tiles_n, tm, tn);
+  const int mwg = tm * 64 * FA, nwg = tn * 64 * FB;
+  const int64_t cpitch = K / 2, spitch = K / 16;
+
+  // Load slots: code loads (2 per fragment) and scale loads (1 per fragment)
+  // dealt round-robin over the 4 waves.  Lane l of a code load fetches the
+  // 16-byte half q of row (32 f + l % 32), k-half l / 32; rows past M / N are
+  // clamped (computed, never stored).
+  const uint8_t* csrc[CPW];
+  int cdst[CPW];
+  const uint8_t* ssrc[SPW];
+  int sdst[SPW];
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int i = wave + 4 * j;  // 0 .. 2 (NFA + NFB) - 1
+    const bool isA = i < 2 * NFA;
+    const int ii = isA ? i : i - 2 * NFA, f = ii >> 1, q = ii & 1;
+    const int row = isA ? min(mwg + 32 * f + li, M - 1) : min(nwg + 32 * f + li, N - 1);
+    csrc[j] = (isA ? ac : bc) + (int64_t)row * cpitch + 32 * hh + 16 * q;
+    cdst[j] = (isA ? 0 : OFF_B) + (2 * f + q) * 1024;
   }
-#undef NVFP4_GEMM_EPI
-#undef NVFP4_GEMM_LAUNCH
-  return hipGetLastError();
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const int i = wave + 4 * j;  // 0 .. NFA + NFB - 1
+    const bool isA = i < NFA;
+    const int f = isA ? i : i - NFA;
+    const int row = isA ? min(mwg + 32 * f + li, M - 1) : min(nwg + 32 * f + li, N - 1);
+    ssrc[j] = (isA ? as : bs) + (int64_t)row * spitch + 4 * hh;
+    sdst[j] = (isA ? OFF_SA : OFF_SB) + f * 256;
+  }
+  auto issue = [&](int kt, int stage) {
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+      __builtin_amdgcn_global_load_lds((gvoid_t*)(csrc[j] + kt / 2), (lvoid_t*)(smem + stage * STAGE + cdst[j]), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+      __builtin_amdgcn_global_load_lds((gvoid_t*)(ssrc[j] + kt / 16), (lvoid_t*)(smem + stage * STAGE + sdst[j]), 4, 0, 0);
+  };
+
+  const int wy = wave >> 1, wx = wave & 1;
+  float16_t acc[FA][FB];
+#pragma unroll
+  for (int i = 0; i < FA; ++i)
+#pragma unroll
+    for (int j = 0; j < FB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nt = K / kKT;
+  issue(0, 0);
+  if (nt > 1) issue(kKT, 1);
+  for (int t = 0; t < nt; ++t) {
+    // This wave's loads of tile t are done once at most the CPW + SPW loads
+    // of tile t + 1 are outstanding; the barrier then publishes every wave's
+    // part of tile t, and guarantees that tile t - 1 (the stage about to be
+    // refilled) has been read by all waves.
+    if (t + 1 < nt) {
+      if constexpr (CPW + SPW == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      else if constexpr (CPW + SPW == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __builtin_amdgcn_s_barrier();
+    if (t + 2 < nt) issue((t + 2) * kKT, (t + 2) % kStages);
+    const uint8_t* st = smem + (t % kStages) * STAGE;
+    Frags<FA, FB> fr;
+#pragma unroll
+    for (int f = 0; f < FA; ++f) {
+      const int fj = wy * FA + f;
+      fr.a[f][0] = *reinterpret_cast<const u32x4_t*>(st + (2 * fj) * 1024 + 16 * l);
+      fr.a[f][1] = *reinterpret_cast<const u32x4_t*>(st + (2 * fj + 1) * 1024 + 16 * l);
+      fr.sa[f] = *reinterpret_cast<const uint32_t*>(st + OFF_SA + fj * 256 + 4 * l);
+    }
+#pragma unroll
+    for (int f = 0; f < FB; ++f) {
+      const int fj = wx * FB + f;
+      fr.b[f][0] = *reinterpret_cast<const u32x4_t*>(st + OFF_B + (2 * fj) * 1024 + 16 * l);
+      fr.b[f][1] = *reinterpret_cast<const u32x4_t*>(st + OFF_B + (2 * fj + 1) * 1024 + 16 * l);
+      fr.sb[f] = *reinterpret_cast<const uint32_t*>(st + OFF_SB + fj * 256 + 4 * l);
+    }
+    compute_tile(fr, acc);
+  }
+  store_tile<FA, FB, OUT, EPI>(acc, ats[0] * bts[0], mwg + wy * 32 * FA, nwg + wx * 32 * FB, li, hh, M, N, c, ldc,
+                               amax_out);
+}
+
+// ---------------------------------------------------------------------------
+// Fallback kernel: any K % 16 == 0 (fragments straight from global memory,
+// bounds-checked along K).
+template <int FA, int FB, int OUT, int EPI>
+__global__ __launch_bounds__(256) void gemm_checked_kernel(
+    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
+    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts,
+    void* __restrict__ c, int64_t ldc, int M, int N, int K, float* __restrict__ amax_out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 31, hh = lane >> 5;
+  const int m0 = blockIdx.y * (64 * FA) + (wave >> 1) * 32 * FA;
+  const int n0 = blockIdx.x * (64 * FB) + (wave & 1) * 32 * FB;
+  const int64_t cpitch = K / 2, spitch = K / 16;
+  const uint8_t* pa[FA];
+  const uint8_t* psa[FA];
+  const uint8_t* pb[FB];
+  const uint8_t* psb[FB];
+#pragma unroll
+  for (int f = 0; f < FA; ++f) {
+    const int row = min(m0 + 32 * f + li, M - 1);
+    pa[f] = ac + (int64_t)row * cpitch + 32 * hh;
+    psa[f] = as + (int64_t)row * spitch + 4 * hh;
+  }
+#pragma unroll
+  for (int f = 0; f < FB; ++f) {
+    const int col = min(n0 + 32 * f + li, N - 1);
+    pb[f] = bc + (int64_t)col * cpitch + 32 * hh;
+    psb[f] = bs + (int64_t)col * spitch + 4 * hh;
+  }
+  float16_t acc[FA][FB];
+#pragma unroll
+  for (int i = 0; i < FA; ++i)
+#pragma unroll
+    for (int j = 0; j < FB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  for (int kt = 0; kt < K; kt += kKT) {
+    // This lane owns k in [kt + 64 hh, kt + 64 hh + 64); code dword s covers
+    // k0 = kt + 64 hh + 8 s (valid iff k0 < K, since K % 16 == 0) and scale
+    // byte q covers k0 = kt + 64 hh + 16 q.
+    const int kl = kt + 64 * hh;
+    Frags<FA, FB> fr;
+    auto ld_codes = [&](const uint8_t* row, u32x4_t (&dst)[2]) {
+      uint32_t w[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) w[s] = (kl + 8 * s < K) ? *reinterpret_cast<const uint32_t*>(row + 4 * s) : 0u;
+      dst[0] = u32x4_t{w[0], w[1], w[2], w[3]};
+      dst[1] = u32x4_t{w[4], w[5], w[6], w[7]};
+    };
+    auto ld_scales = [&](const uint8_t* row) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (kl + 16 * q < K) v |= (uint32_t)row[q] << (8 * q);
+      return v;
+    };
+#pragma unroll
+    for (int f = 0; f < FA; ++f) {
+      ld_codes(pa[f] + kt / 2, fr.a[f]);
+      fr.sa[f] = ld_scales(psa[f] + kt / 16);
+    }
+#pragma unroll
+    for (int f = 0; f < FB; ++f) {
+      ld_codes(pb[f] + kt / 2, fr.b[f]);
+      fr.sb[f] = ld_scales(psb[f] + kt / 16);
+    }
+    compute_tile(fr, acc);
+  }
+  store_tile<FA, FB, OUT, EPI>(acc, ats[0] * bts[0], m0, n0, li, hh, M, N, c, ldc, amax_out);
+}
+
+struct Args {
+  QOut a, b;
+  int m, n, k;
+  void* c;
+  int64_t ldc;
+  float* amax;
+};
+
+template <int FA, int FB, int OUT, int EPI>
+void launch_lds(const Args& g, hipStream_t s) {
+  const int tiles = ((g.m + 64 * FA - 1) / (64 * FA)) * ((g.n + 64 * FB - 1) / (64 * FB));
+  gemm_lds_kernel<FA, FB, OUT, EPI><<<tiles, 256, 0, s>>>(g.a.codes, g.a.scales, g.a.tscale, g.b.codes, g.b.scales,
+                                                          g.b.tscale, g.c, g.ldc, g.m, g.n, g.k, g.amax);
+}
+
+template <int OUT, int EPI>
+void launch_lds_tiles(int fa, int fb, const Args& g, hipStream_t s) {
+  if (fa == 4 && fb == 4) launch_lds<4, 4, OUT, EPI>(g, s);
+  else if (fa == 3 && fb == 3) launch_lds<3, 3, OUT, EPI>(g, s);
+  else if (fa == 4 && fb == 2) launch_lds<4, 2, OUT, EPI>(g, s);
+  else launch_lds<2, 4, OUT, EPI>(g, s);
+}
+
+template <int OUT, int EPI>
+void launch_checked(const Args& g, hipStream_t s) {
+  const dim3 grid((unsigned)((g.n + 255) / 256), (unsigned)((g.m + 127) / 128));
+  gemm_checked_kernel<2, 4, OUT, EPI><<<grid, 256, 0, s>>>(g.a.codes, g.a.scales, g.a.tscale, g.b.codes,
+                                                           g.b.scales, g.b.tscale, g.c, g.ldc, g.m, g.n, g.k, g.amax);
+}
+
+// Tile shape by a small cost model: rounds of 256 workgroups (one per CU) x
+// MFMA work per workgroup / relative efficiency of the shape (bigger
+// fragments amortize the decode over more MFMAs).
+void pick_tiles(int m, int n, int& fa, int& fb) {
+  struct Cand { int fa, fb; double eff; };
+  const Cand cands[] = {{2, 4, 1.0}, {4, 2, 1.0}, {3, 3, 1.05}, {4, 4, 1.15}};
+  double best = 1e300;
+  for (const Cand& cd : cands) {
+    const long tiles = (long)((m + 64 * cd.fa - 1) / (64 * cd.fa)) * ((n + 64 * cd.fb - 1) / (64 * cd.fb));
+    const long rounds = (tiles + 255) / 256;
+    const double cost = (double)rounds * cd.fa * cd.fb / cd.eff;
+    if (cost < best - 1e-9) { best = cost; fa = cd.fa; fb = cd.fb; }
+  }
 }
 
 }  // namespace
 
+bool gemm_tiles_supported(int fa, int fb) {
+  return (fa == 2 && fb == 4) || (fa == 4 && fb == 2) || (fa == 3 && fb == 3) || (fa == 4 && fb == 4);
+}
+
 hipError_t launch_gemm(QOut a, QOut b, int64_t m, int64_t n, int64_t k, void* c, int c_dt,
-                       int64_t ldc, int epilogue, float* amax_out, hipStream_t s) {
+                       int64_t ldc, int epilogue, float* amax_out, int tile_fa, int tile_fb, hipStream_t s) {
   if (amax_out != nullptr) {
     hipError_t e = launch_zero(amax_out, 1, s);
     if (e != hipSuccess) return e;
   }
-  const bool fast = (k % kKT == 0) && ((uintptr_t)a.codes % 16 == 0) && ((uintptr_t)b.codes % 16 == 0) &&
-                    ((uintptr_t)a.scales % 4 == 0) && ((uintptr_t)b.scales % 4 == 0);
-  return launch_tiles<2, 4>(a, b, (int)m, (int)n, (int)k, c, c_dt, ldc, epilogue, amax_out, fast, s);
+  const Args g{a, b, (int)m, (int)n, (int)k, c, ldc, amax_out};
+  const bool lds_path = (k % kKT == 0) && ((uintptr_t)a.codes % 16 == 0) && ((uintptr_t)b.codes % 16 == 0) &&
+                        ((uintptr_t)a.scales % 4 == 0) && ((uintptr_t)b.scales % 4 == 0);
+  if (lds_path) {
+    int fa = tile_fa, fb = tile_fb;
+    if (!gemm_tiles_supported(fa, fb)) pick_tiles((int)m, (int)n, fa, fb);
+    if (c_dt == 0) { if (epilogue == 1) launch_lds_tiles<0, 1>(fa, fb, g, s); else launch_lds_tiles<0, 0>(fa, fb, g, s); }
+    else { if (epilogue == 1) launch_lds_tiles<1, 1>(fa, fb, g, s); else launch_lds_tiles<1, 0>(fa, fb, g, s); }
+  } else {
+    if (c_dt == 0) { if (epilogue == 1) launch_checked<0, 1>(g, s); else launch_checked<0, 0>(g, s); }
+    else { if (epilogue == 1) launch_checked<1, 1>(g, s); else launch_checked<1, 0>(g, s); }
+  }
+  return hipGetLastError();
 }
 
 }  // namespace nvfp4

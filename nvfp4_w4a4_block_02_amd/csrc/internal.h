@@ -17,27 +17,41 @@ struct QOut {            // device pointers of an NVFP4 output / input
 // stays valid inside captured graphs).
 hipError_t launch_zero(float* p, int64_t n, hipStream_t s);
 
-// Step 1: per-domain amax, axis-1 blocks (or plain magnitudes when !rht).
-hipError_t launch_amax_rows(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
-                            int64_t rows_per_domain, float* amax, bool rht, uint32_t mask,
-                            hipStream_t s);
-// Step 1 for RHT along axis 0 (blocks run down columns).
-hipError_t launch_amax_cols_rht(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
-                                float* amax, uint32_t mask, hipStream_t s);
+// Partial maxima: the amax pass writes one float per workgroup and domain;
+// consumers reduce at most kMaxParts of them per domain.
+constexpr uint32_t kMaxParts = 1024;
 
-// Steps 2-6.
+// Number of partials the amax passes below use for a problem.
+uint32_t amax_parts_rows(int64_t rows, int64_t cols, int64_t rows_per_domain);
+uint32_t amax_parts_cols(int64_t rows, int64_t cols);
+
+// Step 1: partial amax per domain, row layout (also used for axis 0 without
+// the transform, where the amax does not depend on the block direction);
+// parts[d * nparts + w].
+hipError_t launch_amax_parts_rows(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
+                                  int64_t rows_per_domain, float* parts, uint32_t nparts, bool rht,
+                                  uint32_t mask, hipStream_t s);
+// Step 1 for blocks running down the columns (one domain), needed with the RHT.
+hipError_t launch_amax_parts_cols(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
+                                  float* parts, uint32_t nparts, bool rht, uint32_t mask, hipStream_t s);
+// Reduce `nparts` partials per domain into amax[ndom].
+hipError_t launch_reduce_parts(const float* parts, uint32_t nparts, int64_t ndom, float* amax, hipStream_t s);
+
+// Steps 2-6 from per-domain partial maxima (nparts = 1: final amax values).
 hipError_t launch_encode_rows(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
-                              int64_t rows_per_domain, const float* amax, QOut out, bool rht,
-                              uint32_t mask, hipStream_t s);
+                              int64_t rows_per_domain, const float* parts, uint32_t nparts, QOut out,
+                              bool rht, uint32_t mask, hipStream_t s);
 hipError_t launch_encode_cols(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
-                              const float* amax, QOut out, bool rht, uint32_t mask, hipStream_t s);
+                              const float* parts, uint32_t nparts, QOut out, bool rht, uint32_t mask,
+                              hipStream_t s);
 
 // Step 7.
 hipError_t launch_dequant(QOut in, int64_t rows, int64_t k, int64_t rows_per_domain, void* out,
                           int out_dt, hipStream_t s);
 
-// Block-scaled GEMM.
+// Block-scaled GEMM; tile_fa/tile_fb = 0 picks the tile shape by cost model.
 hipError_t launch_gemm(QOut a, QOut b, int64_t m, int64_t n, int64_t k, void* c, int c_dt,
-                       int64_t ldc, int epilogue, float* amax_out, hipStream_t s);
+                       int64_t ldc, int epilogue, float* amax_out, int tile_fa, int tile_fb, hipStream_t s);
+bool gemm_tiles_supported(int tile_fa, int tile_fb);
 
 }  // namespace nvfp4

@@ -38,6 +38,12 @@ def test_exports_every_declared_symbol(nv):
         assert hasattr(nv.lib, name), name
 
 
+def test_missing_library_fails_loudly(nv, monkeypatch, tmp_path):
+    monkeypatch.setattr(nv, "LIB_PATH", str(tmp_path / "libnvfp4.so"))
+    with pytest.raises(ImportError, match="no non-HIP fallback"):
+        nv._load()
+
+
 def test_version_and_status_strings(nv):
     assert nv.lib.nvfp4_version() == 10000
     for code, text in [(0, b"ok"), (-1, b"invalid argument"), (-3, b"workspace too small"), (-4, b"HIP launch failed")]:
@@ -46,10 +52,13 @@ def test_version_and_status_strings(nv):
 
 
 def test_workspace_sizes(nv):
-    assert nv.workspace_bytes(nv.OP_QUANTIZE, 10, 32) == 16
+    # 1024 partial maxima (4 KiB) per scaling domain
+    assert nv.workspace_bytes(nv.OP_QUANTIZE, 10, 32) == 4096
+    assert nv.workspace_bytes(nv.OP_RHT16, 10, 32) == 4096
     assert nv.workspace_bytes(nv.OP_GEMM, 10, 32) == 0
-    assert nv.workspace_bytes(nv.OP_KV_QUANT, 12, 8) == 16      # two frame blocks
-    assert nv.workspace_bytes(nv.OP_KV_QUANT, 40, 8) == 32      # five frame blocks
+    assert nv.workspace_bytes(nv.OP_KV_QUANT, 12, 8) == 8192    # two frame blocks
+    assert nv.workspace_bytes(nv.OP_KV_QUANT, 40, 8) == 20480   # five frame blocks
+    assert nv.workspace_bytes(nv.OP_AMAX, 96, 40) == 12288      # three row domains
 
 
 FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced
@@ -69,32 +78,32 @@ def test_quantize_rejects_bad_arguments(nv):
     good = _t(nv, 4, 32)
     EINVAL, EWS = -1, -3
     # null input, bad dtype, k % 16, ld < cols, misaligned x, bad axis, shape mismatch
-    assert q(None, 1, 4, 32, 32, 1, ctypes.byref(good), ws, 16, _stream()) == EINVAL
-    assert q(ctypes.c_void_p(FAKE), 7, 4, 32, 32, 1, ctypes.byref(good), ws, 16, _stream()) == EINVAL
-    assert q(ctypes.c_void_p(FAKE), 1, 4, 40, 40, 1, ctypes.byref(_t(nv, 4, 40)), ws, 16, _stream()) == EINVAL
-    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 16, 1, ctypes.byref(good), ws, 16, _stream()) == EINVAL
-    assert q(ctypes.c_void_p(FAKE + 2), 1, 4, 32, 32, 1, ctypes.byref(good), ws, 16, _stream()) == EINVAL
-    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 36, 1, ctypes.byref(good), ws, 16, _stream()) == EINVAL  # row pitch
-    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 2, ctypes.byref(good), ws, 16, _stream()) == EINVAL
-    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 1, ctypes.byref(_t(nv, 5, 32)), ws, 16, _stream()) == EINVAL
+    assert q(None, 1, 4, 32, 32, 1, ctypes.byref(good), ws, 4096, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 7, 4, 32, 32, 1, ctypes.byref(good), ws, 4096, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 40, 40, 1, ctypes.byref(_t(nv, 4, 40)), ws, 4096, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 16, 1, ctypes.byref(good), ws, 4096, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE + 2), 1, 4, 32, 32, 1, ctypes.byref(good), ws, 4096, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 36, 1, ctypes.byref(good), ws, 4096, _stream()) == EINVAL  # row pitch
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 2, ctypes.byref(good), ws, 4096, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 1, ctypes.byref(_t(nv, 5, 32)), ws, 4096, _stream()) == EINVAL
     # axis 0 needs rows % 16 and a transposed output
-    assert q(ctypes.c_void_p(FAKE), 1, 20, 32, 32, 0, ctypes.byref(_t(nv, 32, 20)), ws, 16, _stream()) == EINVAL
-    assert q(ctypes.c_void_p(FAKE), 1, 32, 48, 48, 0, ctypes.byref(_t(nv, 32, 48)), ws, 16, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 20, 32, 32, 0, ctypes.byref(_t(nv, 32, 20)), ws, 4096, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 32, 48, 48, 0, ctypes.byref(_t(nv, 32, 48)), ws, 4096, _stream()) == EINVAL
     # null / misaligned output pointers
-    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 1, ctypes.byref(_t(nv, 4, 32, codes=0)), ws, 16, _stream()) == EINVAL
-    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 1, ctypes.byref(_t(nv, 4, 32, scales=FAKE + 1)), ws, 16, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 1, ctypes.byref(_t(nv, 4, 32, codes=0)), ws, 4096, _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 1, ctypes.byref(_t(nv, 4, 32, scales=FAKE + 1)), ws, 4096, _stream()) == EINVAL
     # workspace
     assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 1, ctypes.byref(good), None, 16, _stream()) == EINVAL
     assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 1, ctypes.byref(good), ws, 8, _stream()) == EWS
     # zero-sized problems are a no-op (no launch)
-    assert q(ctypes.c_void_p(FAKE), 1, 0, 32, 32, 1, ctypes.byref(_t(nv, 0, 32)), ws, 16, _stream()) == 0
-    assert q(ctypes.c_void_p(FAKE), 1, 4, 0, 0, 1, ctypes.byref(_t(nv, 4, 0)), ws, 16, _stream()) == 0
+    assert q(ctypes.c_void_p(FAKE), 1, 0, 32, 32, 1, ctypes.byref(_t(nv, 0, 32)), ws, 4096, _stream()) == 0
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 0, 0, 1, ctypes.byref(_t(nv, 4, 0)), ws, 4096, _stream()) == 0
 
 
 def test_rht_rejects_wide_mask(nv):
     good = _t(nv, 4, 32)
     st = nv.lib.rht16_quantize(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 1, 1 << 16, ctypes.byref(good),
-                               ctypes.c_void_p(FAKE), 16, _stream())
+                               ctypes.c_void_p(FAKE), 4096, _stream())
     assert st == -1
 
 
@@ -110,16 +119,20 @@ def test_gemm_rejects_bad_arguments(nv):
     assert g(ctypes.byref(a), ctypes.byref(b), c, 0, 16, 0, ctypes.c_void_p(FAKE + 2), None, 0, _stream()) == -1
     assert g(ctypes.byref(_t(nv, 8, 40)), ctypes.byref(_t(nv, 16, 40)), c, 0, 16, 0, None, None, 0, _stream()) == -1
     assert g(ctypes.byref(_t(nv, 0, 64)), ctypes.byref(b), c, 0, 16, 0, None, None, 0, _stream()) == 0
+    gt = nv.lib.nvfp4_gemm_tiled
+    assert gt(ctypes.byref(a), ctypes.byref(b), c, 0, 16, 0, None, 3, 4, _stream()) == -1  # unsupported tiles
+    assert gt(ctypes.byref(a), ctypes.byref(b), c, 0, 8, 0, None, 2, 4, _stream()) == -1   # ldc < N
+    assert gt(ctypes.byref(_t(nv, 0, 64)), ctypes.byref(b), c, 0, 16, 0, None, 4, 4, _stream()) == 0
 
 
 def test_kv_rejects_bad_arguments(nv):
     kq = nv.lib.nvfp4_kv_quant
     out = _t(nv, 12 * 4 * 2, 32)
     ws = ctypes.c_void_p(FAKE)
-    assert kq(ctypes.c_void_p(FAKE), 12, 4, 2, 32, 0, ctypes.byref(out), ws, 16, _stream()) == -1  # frame_block
-    assert kq(ctypes.c_void_p(FAKE), 12, 4, 2, 24, 8, ctypes.byref(_t(nv, 96, 24)), ws, 16, _stream()) == -1
-    assert kq(ctypes.c_void_p(FAKE), 12, 4, 2, 32, 8, ctypes.byref(_t(nv, 95, 32)), ws, 16, _stream()) == -1
-    assert kq(ctypes.c_void_p(FAKE), 40, 4, 2, 32, 8, ctypes.byref(_t(nv, 320, 32)), ws, 16, _stream()) == -3
+    assert kq(ctypes.c_void_p(FAKE), 12, 4, 2, 32, 0, ctypes.byref(out), ws, 4096, _stream()) == -1  # frame_block
+    assert kq(ctypes.c_void_p(FAKE), 12, 4, 2, 24, 8, ctypes.byref(_t(nv, 96, 24)), ws, 4096, _stream()) == -1
+    assert kq(ctypes.c_void_p(FAKE), 12, 4, 2, 32, 8, ctypes.byref(_t(nv, 95, 32)), ws, 4096, _stream()) == -1
+    assert kq(ctypes.c_void_p(FAKE), 40, 4, 2, 32, 8, ctypes.byref(_t(nv, 320, 32)), ws, 4096, _stream()) == -3
     kd = nv.lib.nvfp4_kv_dequant
     assert kd(ctypes.byref(out), 12, 4, 2, 32, 8, None, _stream()) == -1
     assert kd(ctypes.byref(out), 12, 4, 2, 32, 8, ctypes.c_void_p(FAKE + 8), _stream()) == -1
@@ -127,9 +140,13 @@ def test_kv_rejects_bad_arguments(nv):
 
 
 def test_amax_encode_dequant_reject_bad_arguments(nv):
-    assert nv.lib.nvfp4_amax(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 0, None, _stream()) == -1
-    assert nv.lib.nvfp4_amax(ctypes.c_void_p(FAKE), 1, 4, 30, 32, 0, ctypes.c_void_p(FAKE), _stream()) == -1
-    assert nv.lib.nvfp4_amax(ctypes.c_void_p(FAKE), 1, 0, 32, 32, 0, ctypes.c_void_p(FAKE), _stream()) == 0
+    am = nv.lib.nvfp4_amax
+    W = ctypes.c_void_p(FAKE)
+    assert am(W, 1, 4, 32, 32, 0, None, W, 4096, _stream()) == -1
+    assert am(W, 1, 4, 30, 32, 0, W, W, 4096, _stream()) == -1
+    assert am(W, 1, 4, 32, 32, 0, W, None, 4096, _stream()) == -1
+    assert am(W, 1, 8, 32, 32, 4, W, W, 4096, _stream()) == -3    # two domains need 8 KiB
+    assert am(W, 1, 0, 32, 32, 0, W, W, 4096, _stream()) == 0
     good = _t(nv, 64, 32)
     enc = nv.lib.nvfp4_encode
     assert enc(ctypes.c_void_p(FAKE), 1, 64, 32, 32, 1, 0, None, ctypes.byref(good), _stream()) == -1

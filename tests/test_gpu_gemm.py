@@ -51,6 +51,24 @@ def test_gemm_matches_oracle(nv, m, n, k, out):
     assert_gemm_close(c.float().cpu().numpy(), cref, bound, out == "bf16", f"{m}x{n}x{k} {out}")
 
 
+@pytest.mark.parametrize("tiles", [(2, 4), (4, 2), (3, 3), (4, 4)])
+@pytest.mark.parametrize("m,n,k", [(300, 520, 384), (97, 1100, 1280), (1030, 70, 256)])
+def test_gemm_every_tile_shape(nv, tiles, m, n, k):
+    log(f"gemm tiles {tiles} {m}x{n}x{k}")
+    rng = np.random.default_rng(m + n + k + 10 * tiles[0])
+    ga, gb, oa, ob = _operands(nv, rng, m, n, k)
+    cref, bound = oracle.gemm_ref(oa, ob)
+    c = nv.gemm(ga, gb, out_dtype=torch.float32, tiles=tiles)
+    assert_gemm_close(c.cpu().numpy(), cref, bound, False, f"tiles {tiles}")
+    amax = torch.empty(1, device="cuda")
+    h = nv.gemm(ga, gb, out_dtype=torch.bfloat16, epilogue=nv.EPI_GELU_TANH, amax_out=amax, tiles=tiles)
+    hh = h.float().cpu().numpy().astype(np.float64)
+    g = oracle.gelu_tanh(cref)
+    tol = 1.13 * 1e-5 * bound + np.abs(g) * 2.0 ** -8 + 8 * np.spacing(np.abs(g).astype(np.float32)) + 1e-37
+    assert np.all(np.abs(hh - g) <= tol)
+    assert amax.item() == float(np.abs(hh).max())
+
+
 def test_gemm_into_strided_output(nv):
     rng = np.random.default_rng(3)
     ga, gb, oa, ob = _operands(nv, rng, 70, 90, 256)
