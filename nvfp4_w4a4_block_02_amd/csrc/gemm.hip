@@ -28,8 +28,9 @@
 // global->LDS loads (global_load_lds_dwordx4 / _dword).  Every K-tile is read
 // from memory once per workgroup; its LDS image is laid out in the order the
 // consuming lanes read it (fragment, 16-byte half, lane), so the ds_reads are
-// contiguous and conflict-free.  One barrier per K-tile; loads run two tiles
-// ahead.  Decode of step s+1 is interleaved with the MFMAs of step s.
+// contiguous and conflict-free.  One barrier per K-tile; the loads of tile
+// t+3 are spread over the MFMA steps of tile t, and the decode of step s+1 is
+// interleaved with the MFMAs of step s.
 //
 // Fallback kernel (any K % 16 == 0): the same fragments loaded straight into
 // registers with bounds checks; code bytes past K read as 0.
@@ -117,9 +118,11 @@ __device__ __forceinline__ void compute_tile(const Frags<FA, FB>& t, float16_t (
     mfma_step(A0, B0, acc);
     decode_step(t, s + 1, A1, B1);
     interleave_hint<FA, FB>();
+    __builtin_amdgcn_sched_barrier(0);
     mfma_step(A1, B1, acc);
     if (s + 2 < 8) decode_step(t, s + 2, A0, B0);
     interleave_hint<FA, FB>();
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -173,6 +176,64 @@ __device__ __forceinline__ void tile_of(int tiles_n, int ntiles, int& tm, int& t
 
 // ---------------------------------------------------------------------------
 // Main kernel: K % 128 == 0.
+//
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt[5:4] << 14): wait until at most N vector-memory
+// operations of this wave are outstanding / until all LDS reads are done.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+// Per MFMA of one step: one MFMA, its share of the next step's decode, and
+// (for the first NVM MFMAs) one of the global->LDS loads issued in the step.
+// Each step is closed by sched_barrier(0): the interleave is solved per step,
+// which keeps the schedule and makes compilation take seconds instead of the
+// many minutes the solver needs for a whole unrolled tile.
+template <int FA, int FB, int NVM>
+__device__ __forceinline__ void step_schedule() {
+  constexpr int nv = (8 * (FA + FB) + FA * FB - 1) / (FA * FB);
+#pragma unroll
+  for (int i = 0; i < FA * FB; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, nv, 0);  // VALU
+    if (i < NVM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+  }
+}
+
+// Read this wave's fragments of one K-tile from its LDS stage.
+template <int FA, int FB>
+__device__ __forceinline__ void read_stage(Frags<FA, FB>& fr, const uint8_t* st, int wy, int wx, int l,
+                                           int off_b, int off_sa, int off_sb) {
+#pragma unroll
+  for (int f = 0; f < FA; ++f) {
+    const int fj = wy * FA + f;
+    fr.a[f][0] = *reinterpret_cast<const u32x4_t*>(st + (2 * fj) * 1024 + 16 * l);
+    fr.a[f][1] = *reinterpret_cast<const u32x4_t*>(st + (2 * fj + 1) * 1024 + 16 * l);
+    fr.sa[f] = *reinterpret_cast<const uint32_t*>(st + off_sa + fj * 256 + 4 * l);
+  }
+#pragma unroll
+  for (int f = 0; f < FB; ++f) {
+    const int fj = wx * FB + f;
+    fr.b[f][0] = *reinterpret_cast<const u32x4_t*>(st + off_b + (2 * fj) * 1024 + 16 * l);
+    fr.b[f][1] = *reinterpret_cast<const u32x4_t*>(st + off_b + (2 * fj + 1) * 1024 + 16 * l);
+    fr.sb[f] = *reinterpret_cast<const uint32_t*>(st + off_sb + fj * 256 + 4 * l);
+  }
+}
+
+// The ring holds three K-tiles.  Every tile body issues exactly L loads
+// (this wave's share of one future tile), so the wait for "tile t+1 landed"
+// is always vmcnt(L), with no branch on the tile index: near the end of K the
+// loads are clamped to the last tile and land in a stage that is never read
+// again.  Tile body t:
+//   1. wait for this wave's loads of tile t+1 and for its LDS reads of tile t
+//      (already in registers), then one barrier: tile t+1 is complete in LDS
+//      and every wave is done reading stage t % 3;
+//   2. issue the LDS reads of tile t+1 (consumed at the end of the body);
+//   3. 8 MFMA steps on tile t, each overlapped with the decode of the next
+//      step and two of the loads of tile t+3 into stage t % 3.
 template <int FA, int FB, int OUT, int EPI>
 __global__ __launch_bounds__(256) void gemm_lds_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
@@ -184,6 +245,9 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
   static_assert((FA + FB) % 2 == 0, "load slots assume FA + FB even");
   constexpr int CPW = FA + FB;        // 16-byte code loads per wave per tile
   constexpr int SPW = (FA + FB) / 2;  // 4-byte scale loads per wave per tile
+  constexpr int L = CPW + SPW;        // loads per wave per tile
+  constexpr int LPS = (L + 7) / 8;    // loads issued per MFMA step (8 steps per tile)
+  static_assert(3 * L < 64, "three tiles of loads must fit the vmcnt counter");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * STAGE];
 
   const int l = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -199,18 +263,16 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
   // dealt round-robin over the 4 waves.  Lane l of a code load fetches the
   // 16-byte half q of row (32 f + l % 32), k-half l / 32; rows past M / N are
   // clamped (computed, never stored).
-  const uint8_t* csrc[CPW];
-  int cdst[CPW];
-  const uint8_t* ssrc[SPW];
-  int sdst[SPW];
+  const uint8_t* src[L];
+  int dst[L];
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
     const int i = wave + 4 * j;  // 0 .. 2 (NFA + NFB) - 1
     const bool isA = i < 2 * NFA;
     const int ii = isA ? i : i - 2 * NFA, f = ii >> 1, q = ii & 1;
     const int row = isA ? min(mwg + 32 * f + li, M - 1) : min(nwg + 32 * f + li, N - 1);
-    csrc[j] = (isA ? ac : bc) + (int64_t)row * cpitch + 32 * hh + 16 * q;
-    cdst[j] = (isA ? 0 : OFF_B) + (2 * f + q) * 1024;
+    src[j] = (isA ? ac : bc) + (int64_t)row * cpitch + 32 * hh + 16 * q;
+    dst[j] = (isA ? 0 : OFF_B) + (2 * f + q) * 1024;
   }
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
@@ -218,16 +280,15 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
     const bool isA = i < NFA;
     const int f = isA ? i : i - NFA;
     const int row = isA ? min(mwg + 32 * f + li, M - 1) : min(nwg + 32 * f + li, N - 1);
-    ssrc[j] = (isA ? as : bs) + (int64_t)row * spitch + 4 * hh;
-    sdst[j] = (isA ? OFF_SA : OFF_SB) + f * 256;
+    src[CPW + j] = (isA ? as : bs) + (int64_t)row * spitch + 4 * hh;
+    dst[CPW + j] = (isA ? OFF_SA : OFF_SB) + f * 256;
   }
-  auto issue = [&](int kt, int stage) {
-#pragma unroll
-    for (int j = 0; j < CPW; ++j)
-      __builtin_amdgcn_global_load_lds((gvoid_t*)(csrc[j] + kt / 2), (lvoid_t*)(smem + stage * STAGE + cdst[j]), 16, 0, 0);
-#pragma unroll
-    for (int j = 0; j < SPW; ++j)
-      __builtin_amdgcn_global_load_lds((gvoid_t*)(ssrc[j] + kt / 16), (lvoid_t*)(smem + stage * STAGE + sdst[j]), 4, 0, 0);
+  // Load j of tile `tile` into the stage at `st`.
+  auto load = [&](int j, int tile, uint8_t* st) {
+    if (j < CPW)
+      __builtin_amdgcn_global_load_lds((gvoid_t*)(src[j] + (int64_t)tile * (kKT / 2)), (lvoid_t*)(st + dst[j]), 16, 0, 0);
+    else if (j < L)
+      __builtin_amdgcn_global_load_lds((gvoid_t*)(src[j] + (int64_t)tile * (kKT / 16)), (lvoid_t*)(st + dst[j]), 4, 0, 0);
   };
 
   const int wy = wave >> 1, wx = wave & 1;
@@ -240,40 +301,51 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int nt = K / kKT;
-  issue(0, 0);
-  if (nt > 1) issue(kKT, 1);
-  for (int t = 0; t < nt; ++t) {
-    // This wave's loads of tile t are done once at most the CPW + SPW loads
-    // of tile t + 1 are outstanding; the barrier then publishes every wave's
-    // part of tile t, and guarantees that tile t - 1 (the stage about to be
-    // refilled) has been read by all waves.
-    if (t + 1 < nt) {
-      if constexpr (CPW + SPW == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-      else if constexpr (CPW + SPW == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    __builtin_amdgcn_s_barrier();
-    if (t + 2 < nt) issue((t + 2) * kKT, (t + 2) % kStages);
-    const uint8_t* st = smem + (t % kStages) * STAGE;
-    Frags<FA, FB> fr;
 #pragma unroll
-    for (int f = 0; f < FA; ++f) {
-      const int fj = wy * FA + f;
-      fr.a[f][0] = *reinterpret_cast<const u32x4_t*>(st + (2 * fj) * 1024 + 16 * l);
-      fr.a[f][1] = *reinterpret_cast<const u32x4_t*>(st + (2 * fj + 1) * 1024 + 16 * l);
-      fr.sa[f] = *reinterpret_cast<const uint32_t*>(st + OFF_SA + fj * 256 + 4 * l);
-    }
+  for (int t = 0; t < kStages; ++t) {
 #pragma unroll
-    for (int f = 0; f < FB; ++f) {
-      const int fj = wx * FB + f;
-      fr.b[f][0] = *reinterpret_cast<const u32x4_t*>(st + OFF_B + (2 * fj) * 1024 + 16 * l);
-      fr.b[f][1] = *reinterpret_cast<const u32x4_t*>(st + OFF_B + (2 * fj + 1) * 1024 + 16 * l);
-      fr.sb[f] = *reinterpret_cast<const uint32_t*>(st + OFF_SB + fj * 256 + 4 * l);
-    }
-    compute_tile(fr, acc);
+    for (int j = 0; j < L; ++j) load(j, min(t, nt - 1), smem + t * STAGE);
   }
+  wait_vmcnt<2 * L>();  // tile 0 landed (this wave's part)
+  __builtin_amdgcn_s_barrier();
+
+  Frags<FA, FB> F0, F1;
+  half8_t A0[FA], B0[FB], A1[FA], B1[FB];
+  read_stage(F0, smem, wy, wx, l, OFF_B, OFF_SA, OFF_SB);
+  decode_step(F0, 0, A0, B0);
+
+  auto body = [&](int t, const Frags<FA, FB>& cur, Frags<FA, FB>& nxt) {
+    wait_vmcnt<L>();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    read_stage(nxt, smem + ((t + 1) % kStages) * STAGE, wy, wx, l, OFF_B, OFF_SA, OFF_SB);
+    uint8_t* const ist = smem + (t % kStages) * STAGE;
+    const int tl = min(t + kStages, nt - 1);
+#pragma unroll
+    for (int s = 0; s < 8; s += 2) {
+      mfma_step(A0, B0, acc);
+#pragma unroll
+      for (int q = 0; q < LPS; ++q) load(s * LPS + q, tl, ist);
+      decode_step(cur, s + 1, A1, B1);
+      step_schedule<FA, FB, LPS>();
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(A1, B1, acc);
+#pragma unroll
+      for (int q = 0; q < LPS; ++q) load((s + 1) * LPS + q, tl, ist);
+      if (s + 2 < 8) decode_step(cur, s + 2, A0, B0);
+      else decode_step(nxt, 0, A0, B0);
+      step_schedule<FA, FB, LPS>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  int t = 0;
+  for (; t + 2 <= nt; t += 2) {
+    body(t, F0, F1);
+    body(t + 1, F1, F0);
+  }
+  if (t < nt) body(t, F0, F1);
+  wait_vmcnt<0>();  // no load into LDS may be in flight when the workgroup ends
+
   store_tile<FA, FB, OUT, EPI>(acc, ats[0] * bts[0], mwg + wy * 32 * FA, nwg + wx * 32 * FB, li, hh, M, N, c, ldc,
                                amax_out);
 }
