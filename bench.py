@@ -106,7 +106,7 @@ def bench_attn_proj(nv, torch, wl, steps, warmup, nsets):
         sets.append({
             "x": x, "wq": wq,
             "xq": nv.NVFP4Tensor.empty(m, k, 1, "cuda"),
-            "ws": torch.empty(1024, device="cuda"),
+            "ws": nv._workspace(nv.OP_QUANTIZE, m, k, "cuda"),
             "y": torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
         })
     stream = torch.cuda.current_stream()
@@ -177,7 +177,7 @@ def bench_rows(nv, torch, wl, steps, warmup):
             s[nm] = _dev_bf16(torch, d[nm]).reshape(shape)
             s[nm + "q"] = nv.NVFP4Tensor.empty(12 * 880 * 24, 128, 2, "cuda")
             s[nm + "o"] = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
-        s["ws"] = torch.empty(2048, device="cuda")
+        s["ws"] = nv._workspace(nv.OP_KV_QUANT, 12, 8, "cuda")
         kvsets.append(s)
 
     def kvq(s, t):
@@ -207,7 +207,7 @@ def bench_rows(nv, torch, wl, steps, warmup):
     rsets = []
     for i in range(3):
         s = {"g": _dev_bf16(torch, d["g"]), "x": _dev_bf16(torch, d["x"]),
-             "gq": nv.NVFP4Tensor.empty(cols, rows, 1, "cuda"), "ws": torch.empty(1024, device="cuda")}
+             "gq": nv.NVFP4Tensor.empty(cols, rows, 1, "cuda"), "ws": nv._workspace(nv.OP_RHT16, rows, cols, "cuda")}
         s["xq"] = nv.rht16_quantize(s["x"], d["mask"], axis=0)
         s["c"] = torch.empty((cols, cols), dtype=torch.float32, device="cuda")
         rsets.append(s)
@@ -237,7 +237,7 @@ def bench_rows(nv, torch, wl, steps, warmup):
     x = _dev_bf16(torch, d["x"])
     w1 = nv.quantize(torch.from_numpy(d["w1"]).cuda())
     w2 = nv.quantize(torch.from_numpy(d["w2"]).cuda())
-    bufs = {"xq": nv.NVFP4Tensor.empty(m, dm, 1, "cuda"), "ws": torch.empty(1024, device="cuda"),
+    bufs = {"xq": nv.NVFP4Tensor.empty(m, dm, 1, "cuda"), "ws": nv._workspace(nv.OP_QUANTIZE, m, dm, "cuda"),
             "h": torch.empty((m, f), dtype=torch.float32, device="cuda"),
             "hmax": torch.empty(1, device="cuda"), "hq": nv.NVFP4Tensor.empty(m, f, 1, "cuda"),
             "y": torch.empty((m, dm), dtype=torch.bfloat16, device="cuda")}

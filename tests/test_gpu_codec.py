@@ -233,3 +233,22 @@ def test_full_rht_gradient(nv):
     oq = oracle.rht16_quantize(widen(d["g"]), d["mask"], axis=0)
     torch.cuda.synchronize()
     assert_q_exact(gq, oq, "rht G")
+
+
+
+@pytest.mark.parametrize("rht", [False, True])
+def test_workspace_shared_by_consecutive_calls(nv, rht):
+    """Calls that reuse one workspace (stream-ordered) each see only their
+    own partial maxima: the second call on different data is still exact."""
+    rng = np.random.default_rng(61 + rht)
+    mask = 0xA5C3
+    ws = torch.empty((nv.workspace_bytes(nv.OP_QUANTIZE, 700, 3072) // 4,), dtype=torch.float32, device="cuda")
+    for scale in (1.0, 1e-3):
+        x = (_rand(rng, 700, 3072) * np.float32(scale)).astype(np.float32)
+        bits = host_bf16_bits(torch.from_numpy(x).to(torch.bfloat16))
+        want = oracle.rht16_quantize(widen(bits), mask) if rht else oracle.quantize(widen(bits))
+        xd = dev_bf16(bits)
+        log(f"shared workspace rht={rht} scale={scale}")
+        gq = nv.rht16_quantize(xd, mask, ws=ws) if rht else nv.quantize(xd, ws=ws)
+        torch.cuda.synchronize()
+        assert_q_exact(gq, want, f"rht={rht} scale={scale}")
