@@ -17,8 +17,10 @@
 //     workgroup of the encode pass reduces its domain's partials (at most
 //     kMaxParts floats, an L2 hit) before it starts;
 //   * column mode (blocks running down the columns, output stored
-//     transposed) goes through an LDS tile so that both the reads and the
-//     8-byte code writes stay coalesced.
+//     transposed): each thread loads a 4-column chunk from 16 consecutive
+//     rows, i.e. four whole blocks, straight into registers; only the
+//     encoded output is staged in LDS, so that the transposed code and
+//     scale writes stay contiguous.
 #include "device.h"
 #include "internal.h"
 
@@ -155,104 +157,126 @@ __global__ __launch_bounds__(kThreads) void encode_rows_kernel(
 // ---------------------------------------------------------------------------
 // Column layout (axis 0): x is [rows][ld], 16-element blocks run down the
 // columns and the NVFP4 output is the transpose ([cols][rows/2] codes,
-// [cols][rows/16] scales).  One tile = 128 rows (8 blocks) x 64 columns:
-//   1. coalesced 16-byte loads of the tile into LDS (as float32);
-//   2. thread t transforms/encodes blocks (column t % 64, block t / 64 and
-//      t / 64 + 4), reading a column of LDS (conflict-free: consecutive lanes,
-//      consecutive words);
-//   3. the 8-byte codes and the scale bytes are staged in LDS and written so
-//      that consecutive lanes fill consecutive bytes of an output row.
-// AMAX_ONLY: step 1 of the recipe for the transformed tensor (no output but
-// one partial max per workgroup).
-constexpr int kTR = 128;  // tile rows (reduction dim)
-constexpr int kTC = 64;   // tile columns
+// [cols][rows/16] scales).  One tile = kColRB row blocks (128 rows) x 128
+// columns.  Thread t owns column chunk t % 32 (4 consecutive columns) of row
+// block t / 32: it loads the chunk from each of the block's 16 rows (8-byte
+// loads for bf16, 16-byte for float32; a wavefront reads two 256- or
+// 512-byte row segments per load), so it holds four complete column blocks
+// in registers — no transpose through LDS is needed to compute them.  Only
+// the encoded output goes through LDS, so that every column's codes (64
+// bytes) and scales (8 bytes) of the tile are written contiguously.
+// AMAX_ONLY: step 1 of the recipe for the (transformed) tensor, one partial
+// maximum per workgroup.
+constexpr int kColRB = 8;                       // row blocks per tile
+constexpr int kColCH = kThreads / kColRB;       // column chunks per tile
+constexpr int kColCPC = 4;                      // columns per chunk
+constexpr int kColTC = kColCH * kColCPC;        // tile columns
+constexpr int kColTR = kColRB * kBlock;         // tile rows
+
+template <int DT>
+struct ColChunk;
+template <>
+struct ColChunk<1> { u32x2_t v; };   // 4 bf16
+template <>
+struct ColChunk<0> { float4_t v; };  // 4 float32
+
+template <int DT>
+__device__ __forceinline__ float chunk_elem(const ColChunk<DT>& c, int j) {
+  if constexpr (DT == 1) {
+    const uint32_t w = (j < 2) ? c.v.x : c.v.y;
+    return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  } else {
+    return j == 0 ? c.v.x : j == 1 ? c.v.y : j == 2 ? c.v.z : c.v.w;
+  }
+}
 
 template <int DT, bool RHT, bool AMAX_ONLY>
-__global__ __launch_bounds__(kThreads) void cols_tile_kernel(
+__global__ __launch_bounds__(kThreads) void cols_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     const float* __restrict__ parts_in, int nparts_in, float* __restrict__ parts_out,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ tscale,
     uint32_t mask) {
-  __shared__ float tile[kTR][kTC + 1];
-  __shared__ u32x2_t ocodes[kTC][kTR / 16];
-  __shared__ uint8_t oscale[kTC][kTR / 16];
+  // Output staging, row-block major with one column of padding so that both
+  // the per-thread writes and the per-column reads spread over the banks.
+  __shared__ u32x2_t ocodes[AMAX_ONLY ? 1 : kColRB][kColTC + 1];
+  __shared__ uint8_t oscale[AMAX_ONLY ? 1 : kColRB][kColTC + 4];
   float S = 0.0f;
   if constexpr (!AMAX_ONLY) {
     S = reduce_parts(parts_in, nparts_in) / kGlobalMax;
     if (blockIdx.x == 0 && threadIdx.x == 0) tscale[0] = S;
   }
   const int64_t nbc = rows / kBlock;               // blocks per column = per output row
-  const uint32_t ntr = cdiv(rows, kTR), ntc = cdiv(cols, kTC);
+  const uint32_t ntr = cdiv(rows, kColTR), ntc = cdiv(cols, kColTC);
   const uint32_t ntiles = ntr * ntc;
-  const int t = threadIdx.x;
-  constexpr int kEpc = 16 / (DT == 0 ? 4 : 2);     // elements per 16-byte chunk
-  constexpr int kCpr = kTC / kEpc;                 // chunks per tile row
-  const bool vec_ok = (cols % kEpc) == 0;          // every chunk fully inside or outside
+  const int t = threadIdx.x, q = t % kColCH, rb = t / kColCH;
   float m = 0.0f;
   for (uint32_t tl = blockIdx.x; tl < ntiles; tl += gridDim.x) {
     const int64_t tr = tl / ntc, tc = tl - tr * ntc;
-    const int64_t k0 = tr * kTR, c0 = tc * kTC;
-    const int nrow = (int)(rows - k0 < kTR ? rows - k0 : kTR);  // multiple of 16
-    __syncthreads();  // previous tile's LDS reads are done
-    for (int q = t; q < kTR * kCpr; q += kThreads) {
-      const int r = q / kCpr, ch = q - r * kCpr;
-      const int64_t c = c0 + (int64_t)ch * kEpc;
-      float v[kEpc];
-      if (r < nrow && c + kEpc <= cols && vec_ok) {
-        const int64_t off = (k0 + r) * ld + c;
-        if constexpr (DT == 0) {
-          const float4_t u = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(static_cast<const float*>(x) + off));
-          v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
-        } else {
-          const u32x4_t u = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(x) + off));
-          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const int64_t k0 = tr * kColTR, c0 = tc * kColTC;
+    const int nb = (int)((rows - k0) / kBlock < kColRB ? (rows - k0) / kBlock : kColRB);  // row blocks present
+    const int64_t r0 = k0 + (int64_t)rb * kBlock;
+    const int64_t cq = c0 + (int64_t)q * kColCPC;
+    const bool active = rb < nb && cq < cols;
+    ColChunk<DT> raw[kBlock];
+    if (active) {
+      if (cq + kColCPC <= cols) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            v[2 * j] = __uint_as_float(w[j] << 16);
-            v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+        for (int i = 0; i < kBlock; ++i) {
+          const int64_t off = (r0 + i) * ld + cq;
+          if constexpr (DT == 1)
+            raw[i].v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(x) + off));
+          else
+            raw[i].v = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(static_cast<const float*>(x) + off));
+        }
+      } else {  // right edge: columns past `cols` read as 0 (their blocks are skipped)
+#pragma unroll
+        for (int i = 0; i < kBlock; ++i) {
+          const int64_t off = (r0 + i) * ld + cq;
+          float e[kColCPC];
+#pragma unroll
+          for (int j = 0; j < kColCPC; ++j) e[j] = cq + j < cols ? load1<DT>(x, off + j) : 0.0f;
+          if constexpr (DT == 1) {
+            raw[i].v = u32x2_t{(__float_as_uint(e[0]) >> 16) | (__float_as_uint(e[1]) & 0xFFFF0000u),
+                               (__float_as_uint(e[2]) >> 16) | (__float_as_uint(e[3]) & 0xFFFF0000u)};
+          } else {
+            raw[i].v = float4_t{e[0], e[1], e[2], e[3]};
           }
         }
-      } else {
-#pragma unroll
-        for (int j = 0; j < kEpc; ++j)
-          v[j] = (r < nrow && c + j < cols) ? load1<DT>(x, (k0 + r) * ld + c + j) : 0.0f;
       }
-#pragma unroll
-      for (int j = 0; j < kEpc; ++j) tile[r][ch * kEpc + j] = v[j];
     }
-    __syncthreads();
-    const int cc = t & (kTC - 1);
+    if constexpr (!AMAX_ONLY) __syncthreads();  // the previous tile's output is written out
+    if (active) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int jb = (t >> 6) + 4 * h;  // block within the tile
-      if (16 * jb >= nrow || c0 + cc >= cols) continue;
-      float v[16];
+      for (int j = 0; j < kColCPC; ++j) {
+        if (cq + j >= cols) break;
+        float v[kBlock];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = tile[16 * jb + i][cc];
-      if constexpr (RHT) rht16(v, mask);
-      float a = 0.0f;
+        for (int i = 0; i < kBlock; ++i) v[i] = chunk_elem<DT>(raw[i], j);
+        if constexpr (RHT) rht16(v, mask);
+        float a = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
-      if constexpr (AMAX_ONLY) {
-        m = fmaxf(m, a);
-      } else {
-        float rcp;
-        const uint32_t sig = block_scale(a, S, rcp);
-        ocodes[cc][jb] = encode16(v, rcp);
-        oscale[cc][jb] = (uint8_t)sig;
+        for (int i = 0; i < kBlock; ++i) a = fmaxf(a, fabsf(v[i]));
+        if constexpr (AMAX_ONLY) {
+          m = fmaxf(m, a);
+        } else {
+          float rcp;
+          const uint32_t sig = block_scale(a, S, rcp);
+          ocodes[rb][q * kColCPC + j] = encode16(v, rcp);
+          oscale[rb][q * kColCPC + j] = (uint8_t)sig;
+        }
       }
     }
     if constexpr (!AMAX_ONLY) {
       __syncthreads();
-      const int nb = nrow / 16;
+      // Consecutive threads write consecutive blocks of one output row.
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int p = t + kThreads * h;  // (output row, block) pair
-        const int orow = p >> 3, b = p & 7;
-        if (b < nb && c0 + orow < cols) {
-          const int64_t ob = (c0 + orow) * nbc + k0 / 16 + b;  // block index in the output
-          reinterpret_cast<u32x2_t*>(codes)[ob] = ocodes[orow][b];
-          scales[ob] = oscale[orow][b];
+      for (int h = 0; h < kColTC * kColRB / kThreads; ++h) {
+        const int p = t + kThreads * h;
+        const int col = p / kColRB, b = p % kColRB;
+        if (b < nb && c0 + col < cols) {
+          const int64_t ob = (c0 + col) * nbc + k0 / kBlock + b;  // block index in the output
+          reinterpret_cast<u32x2_t*>(codes)[ob] = ocodes[b][col];
+          scales[ob] = oscale[b][col];
         }
       }
     }
@@ -264,38 +288,48 @@ __global__ __launch_bounds__(kThreads) void cols_tile_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Step 7: x' = f32(e2m1 * s_b) * S, then float32 or bf16 (RNE) out.
+// Step 7: x' = f32(e2m1 * s_b) * S, then float32 or bf16 (RNE) out.  The
+// unit of work is one 16-byte piece of output — 8 bf16 (one code dword) or 4
+// float32 (one code half-word) — so that consecutive lanes store consecutive
+// 16 bytes (one contiguous 1 KiB per wavefront store) and load consecutive
+// code bytes.  Four units are in flight per thread.
 template <int OUT>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ ts, int64_t rows, int64_t k, int64_t rpd, void* __restrict__ out) {
-  const uint32_t bpr = (uint32_t)(k / kBlock);
-  const uint32_t nblk = (uint32_t)(rows * bpr);
+  constexpr int E = OUT == 1 ? 8 : 4;                  // elements per unit
+  const uint64_t nunits = (uint64_t)rows * (uint64_t)k / E;
+  const uint64_t upd = (uint64_t)(rpd < rows ? rpd : rows) * (uint64_t)k / E;  // units per domain
   const bool one_domain = (rpd >= rows);
-  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < nblk; i += gridDim.x * kThreads) {
-    const uint32_t dom = one_domain ? 0u : (i / bpr) / (uint32_t)rpd;
-    const float S = ts[dom];
-    const u32x2_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(codes) + i);
-    const float sf = e4m3_to_f32(scales[i]);
-    float o[16];
-    decode8_f32(w.x, o);
-    decode8_f32(w.y, o + 8);
+  const bool narrow = nunits <= 0xFFFFFFFFull;  // 32-bit domain division suffices
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  auto unit = [&](uint64_t u) {
+    const uint64_t d = one_domain ? 0 : narrow ? (uint64_t)((uint32_t)u / (uint32_t)upd) : u / upd;
+    const float S = ts[d];
+    const float sf = e4m3_to_f32(scales[u * E / kBlock]);
+    if constexpr (OUT == 1) {
+      float o[8];
+      decode8_f32(__builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(codes) + u), o);
+      uint32_t p[4];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[e] = (o[e] * sf) * S;
-    if constexpr (OUT == 0) {
-      float4_t* dst = reinterpret_cast<float4_t*>(out) + (int64_t)i * 4;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        __builtin_nontemporal_store(float4_t{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]}, dst + q);
+      for (int q = 0; q < 4; ++q) p[q] = f32_to_bf16_rne((o[2 * q] * sf) * S) | (f32_to_bf16_rne((o[2 * q + 1] * sf) * S) << 16);
+      __builtin_nontemporal_store(u32x4_t{p[0], p[1], p[2], p[3]}, reinterpret_cast<u32x4_t*>(out) + u);
     } else {
-      uint32_t p[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) p[q] = f32_to_bf16_rne(o[2 * q]) | (f32_to_bf16_rne(o[2 * q + 1]) << 16);
-      u32x4_t* dst = reinterpret_cast<u32x4_t*>(out) + (int64_t)i * 2;
-      __builtin_nontemporal_store(u32x4_t{p[0], p[1], p[2], p[3]}, dst);
-      __builtin_nontemporal_store(u32x4_t{p[4], p[5], p[6], p[7]}, dst + 1);
+      const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(codes) + u);
+      const float2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+      const float2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+      __builtin_nontemporal_store(float4_t{(a.x * sf) * S, (a.y * sf) * S, (b.x * sf) * S, (b.y * sf) * S},
+                                  reinterpret_cast<float4_t*>(out) + u);
     }
+  };
+  uint64_t u = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; u + 3 * stride < nunits; u += 4 * stride) {
+    unit(u);
+    unit(u + stride);
+    unit(u + 2 * stride);
+    unit(u + 3 * stride);
   }
+  for (; u < nunits; u += stride) unit(u);
 }
 
 __global__ __launch_bounds__(kThreads) void reduce_parts_kernel(const float* __restrict__ parts, int nparts,
@@ -304,19 +338,20 @@ __global__ __launch_bounds__(kThreads) void reduce_parts_kernel(const float* __r
   if (threadIdx.x == 0) amax[blockIdx.x] = m;
 }
 
-// Partial-max workgroups for `nblk` 16-element blocks: about 8 blocks per
-// thread, capped at kMaxParts.
+// Partial-max workgroups for `nblk` 16-element blocks: about 4 blocks per
+// thread (enough workgroups to keep HBM busy on small tensors), capped at
+// kMaxParts.
 inline uint32_t parts_for(int64_t nblk) {
-  int64_t p = (nblk + 8 * kThreads - 1) / (8 * kThreads);
+  int64_t p = (nblk + 4 * kThreads - 1) / (4 * kThreads);
   if (p < 1) p = 1;
   return (uint32_t)(p < kMaxParts ? p : kMaxParts);
 }
 
 // Encode workgroups per domain: two blocks per thread per iteration, at most
-// 256 CUs x 8 workgroups over all domains.
+// 256 CUs x 16 workgroups over all domains.
 inline uint32_t encode_grid(int64_t nblk, int64_t ndom) {
   int64_t g = (nblk + 2 * kThreads - 1) / (2 * kThreads);
-  const int64_t cap = (2048 + ndom - 1) / ndom;
+  const int64_t cap = (4096 + ndom - 1) / ndom;
   if (g > cap) g = cap;
   return (uint32_t)(g < 1 ? 1 : g);
 }
@@ -341,7 +376,7 @@ uint32_t amax_parts_rows(int64_t rows, int64_t cols, int64_t rpd) {
 }
 
 uint32_t amax_parts_cols(int64_t rows, int64_t cols) {
-  const int64_t tiles = (int64_t)cdiv(rows, kTR) * cdiv(cols, kTC);
+  const int64_t tiles = (int64_t)cdiv(rows, kColTR) * cdiv(cols, kColTC);
   return (uint32_t)(tiles < kMaxParts ? (tiles < 1 ? 1 : tiles) : kMaxParts);
 }
 
@@ -360,7 +395,7 @@ hipError_t launch_amax_parts_rows(const void* x, int dt, int64_t rows, int64_t c
 hipError_t launch_amax_parts_cols(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
                                   float* parts, uint32_t nparts, bool rht, uint32_t mask, hipStream_t s) {
 #define NVFP4_CAMAX(D, R)                                                                        \
-  cols_tile_kernel<D, R, true><<<nparts, kThreads, 0, s>>>(x, rows, cols, ld, nullptr, 0, parts, \
+  cols_kernel<D, R, true><<<nparts, kThreads, 0, s>>>(x, rows, cols, ld, nullptr, 0, parts, \
                                                             nullptr, nullptr, nullptr, mask)
   if (dt == 0) { if (rht) NVFP4_CAMAX(0, true); else NVFP4_CAMAX(0, false); }
   else { if (rht) NVFP4_CAMAX(1, true); else NVFP4_CAMAX(1, false); }
@@ -386,10 +421,12 @@ hipError_t launch_encode_rows(const void* x, int dt, int64_t rows, int64_t cols,
 hipError_t launch_encode_cols(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
                               const float* parts, uint32_t nparts, QOut out, bool rht, uint32_t mask,
                               hipStream_t s) {
-  const int64_t tiles = (int64_t)cdiv(rows, kTR) * cdiv(cols, kTC);
-  const unsigned grid = (unsigned)(tiles < 2048 ? tiles : 2048);
+  // Same grid as the amax pass: at most kMaxParts workgroups, so that a
+  // tensor of many tiles gives every workgroup the same number of them.
+  const int64_t tiles = (int64_t)cdiv(rows, kColTR) * cdiv(cols, kColTC);
+  const unsigned grid = (unsigned)(tiles < (int64_t)kMaxParts ? tiles : kMaxParts);
 #define NVFP4_ENC_COLS(D, R)                                                                     \
-  cols_tile_kernel<D, R, false><<<grid, kThreads, 0, s>>>(x, rows, cols, ld, parts, (int)nparts, \
+  cols_kernel<D, R, false><<<grid, kThreads, 0, s>>>(x, rows, cols, ld, parts, (int)nparts, \
                                                           nullptr, out.codes, out.scales,        \
                                                           out.tscale, mask)
   if (dt == 0) { if (rht) NVFP4_ENC_COLS(0, true); else NVFP4_ENC_COLS(0, false); }
@@ -401,7 +438,8 @@ hipError_t launch_encode_cols(const void* x, int dt, int64_t rows, int64_t cols,
 hipError_t launch_dequant(QOut in, int64_t rows, int64_t k, int64_t rpd, void* out, int out_dt,
                           hipStream_t s) {
   if (rpd <= 0 || rpd > rows) rpd = rows;
-  int64_t g = (rows * (k / kBlock) + kThreads - 1) / kThreads;
+  const int64_t units = rows * k / (out_dt == 0 ? 4 : 8);
+  int64_t g = (units + 4 * kThreads - 1) / (4 * kThreads);
   const unsigned grid = (unsigned)(g < 4096 ? (g < 1 ? 1 : g) : 4096);
   if (out_dt == 0) dequant_kernel<0><<<grid, kThreads, 0, s>>>(in.codes, in.scales, in.tscale, rows, k, rpd, out);
   else dequant_kernel<1><<<grid, kThreads, 0, s>>>(in.codes, in.scales, in.tscale, rows, k, rpd, out);
