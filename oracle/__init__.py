@@ -25,7 +25,9 @@ Sources.  The format is defined by the LongLive-2.0 pages:
   largo", section "Entrenamiento NVFP4": the block scale is FP8 and the tensor
   scale FP32; RHT is applied before quantization on gradient-sensitive paths.
   Section "Inferencia W4A4 NVFP4": FP4 GEMMs replace the BF16 GEMMs and the KV
-  cache uses the same format (about 3.6x smaller than bf16).
+  cache uses the same format (about 3.6x smaller than bf16), with an adaptive
+  scale selection named Four Over Six (``four_over_six.py`` states the
+  reading).
 * hyper.ai summary of the LongLive-2.0 paper, section "方法": the KV cache is
   quantized per block of eight frames and rebuilt by a parallel dequant kernel.
 
@@ -65,3 +67,10 @@ from .codec import (  # noqa: F401
 )
 from .rht import hadamard16, sign_vector, rht16_rows, rht16_quantize  # noqa: F401
 from .gemm import gemm_ref, gelu_tanh, ffn_chain  # noqa: F401
+from .four_over_six import (  # noqa: F401
+    block_scales_to,
+    block_sq_error,
+    quantize_4over6,
+    quantize_4over6_with_amax,
+    kv_quantize_4over6,
+)
