@@ -16,7 +16,8 @@ Besides the headline value the line carries:
   cpu_baseline  the CPU oracle timed on a bounded sample of the same
                 workload on this host;
   rows          the other rows of the path, each timed the same way: KV codec
-                quantize/dequantize (12x880x24x128 bf16, K and V), RHT16 +
+                quantize (core recipe and Four Over Six) and dequantize
+                (12x880x24x128 bf16, K and V), RHT16 +
                 quantize of a 16384x3072 gradient along dim 0, the 3072x3072x
                 16384 weight-gradient GEMM, and the FFN pair
                 (10560x3072 -> 14336 -> 3072).
@@ -186,6 +187,12 @@ def bench_rows(nv, torch, wl, steps, warmup):
         nv.kv_quant(s["v"], out=s["vq"], ws=s["ws"], stream=stream)
         if t: t.stop()
 
+    def kvq6(s, t):
+        if t: t.start()
+        nv.kv_quant(s["k"], out=s["kq"], ws=s["ws"], stream=stream, four_over_six=True)
+        nv.kv_quant(s["v"], out=s["vq"], ws=s["ws"], stream=stream, four_over_six=True)
+        if t: t.stop()
+
     def kvd(s, t):
         if t: t.start()
         nv.kv_dequant(s["kq"], shape, out=s["ko"], stream=stream)
@@ -197,6 +204,9 @@ def bench_rows(nv, torch, wl, steps, warmup):
     ms = _time_loop(torch, kvq, kvsets, steps, warmup)
     out["kv_quant"] = {"ms": ms, "GB/s": kv_bytes / ms / 1e6, "frac_hbm": kv_bytes / ms / 1e6 / HBM_PEAK_GBS,
                        "bytes": kv_bytes}
+    ms = _time_loop(torch, kvq6, kvsets, steps, warmup)
+    out["kv_quant_4over6"] = {"ms": ms, "GB/s": kv_bytes / ms / 1e6,
+                              "frac_hbm": kv_bytes / ms / 1e6 / HBM_PEAK_GBS, "bytes": kv_bytes}
     ms = _time_loop(torch, kvd, kvsets, steps, warmup)
     out["kv_dequant"] = {"ms": ms, "GB/s": kv_bytes / ms / 1e6, "frac_hbm": kv_bytes / ms / 1e6 / HBM_PEAK_GBS,
                          "bytes": kv_bytes}

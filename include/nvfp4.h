@@ -204,6 +204,23 @@ int nvfp4_kv_quant(const void *kv, int64_t frames, int64_t tokens, int64_t heads
                    void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * nvfp4_kv_quant with the Four Over Six encoder (tailorednewshub.com,
+ * "Inferencia W4A4 NVFP4": the NVFP4 KV cache uses adaptive scale selection
+ * under that name; the pages give nothing beyond the name).  Reading
+ * implemented: same format, tensor scales and decode as nvfp4_kv_quant; for
+ * every 16-element block two candidates are encoded, one whose scale maps the
+ * block maximum to 6 (the core recipe) and one mapping it to 4
+ * (s_b = E4M3((max|x| / 4) / S)), and the stored one is the candidate with
+ * the strictly smaller squared decode error
+ * E = sum_i (x_i - f32(e2m1_i * s_b) * S)^2, each operation a separately
+ * rounded float32 operation summed from element 0 to 15 (ties keep the core
+ * recipe).  Arguments, layout, workspace and errors as nvfp4_kv_quant.
+ */
+int nvfp4_kv_quant_4over6(const void *kv, int64_t frames, int64_t tokens, int64_t heads,
+                          int64_t head_dim, int64_t frame_block, const nvfp4_tensor *out,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/*
  * KV-cache dequantization of the whole window to bf16 (the pages rebuild the
  * cache with a parallel dequant kernel for window attention: hyper.ai
  * summary, section "方法").  out: device bf16 [frames][tokens][heads][head_dim].

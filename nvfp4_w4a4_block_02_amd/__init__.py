@@ -60,6 +60,7 @@ def _load():
         "nvfp4_gemm": (I, [TP, TP, P, I, I64, I, P, P, SZ, P]),
         "nvfp4_gemm_tiled": (I, [TP, TP, P, I, I64, I, P, I, I, P]),
         "nvfp4_kv_quant": (I, [P, I64, I64, I64, I64, I64, TP, P, SZ, P]),
+        "nvfp4_kv_quant_4over6": (I, [P, I64, I64, I64, I64, I64, TP, P, SZ, P]),
         "nvfp4_kv_dequant": (I, [TP, I64, I64, I64, I64, I64, P, P]),
         "nvfp4_dequantize": (I, [TP, I64, P, I, P]),
     }
@@ -88,7 +89,7 @@ def __getattr__(name):  # module attribute `lib` loads the library on first acce
 
 EXPORTED = ("nvfp4_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_amax",
             "nvfp4_encode", "nvfp4_quantize", "rht16_quantize", "nvfp4_gemm", "nvfp4_gemm_tiled", "nvfp4_kv_quant",
-            "nvfp4_kv_dequant", "nvfp4_dequantize")
+            "nvfp4_kv_quant_4over6", "nvfp4_kv_dequant", "nvfp4_dequantize")
 
 
 def _check(status: int, what: str):
@@ -239,7 +240,9 @@ def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.bfloat16, epilogue: int
 
 
 def kv_quant(kv: torch.Tensor, frame_block: int = 8, out: NVFP4Tensor | None = None,
-             ws: torch.Tensor | None = None, stream=None) -> NVFP4Tensor:
+             ws: torch.Tensor | None = None, stream=None, four_over_six: bool = False) -> NVFP4Tensor:
+    """KV-cache quantization in frame blocks; ``four_over_six`` selects the
+    Four Over Six encoder (nvfp4_kv_quant_4over6)."""
     f, t, h, d = kv.shape
     if kv.dtype != torch.bfloat16 or not kv.is_contiguous():
         raise TypeError("kv must be a contiguous bfloat16 tensor [frames, tokens, heads, head_dim]")
@@ -249,8 +252,9 @@ def kv_quant(kv: torch.Tensor, frame_block: int = 8, out: NVFP4Tensor | None = N
     if ws is None:
         ws = _workspace(OP_KV_QUANT, f, frame_block, kv.device)
     ct = out.c()
-    _check(_lib().nvfp4_kv_quant(_ptr(kv), f, t, h, d, frame_block, ctypes.byref(ct), _ptr(ws), ws.numel() * 4,
-                              _stream(stream)), "nvfp4_kv_quant")
+    fn = _lib().nvfp4_kv_quant_4over6 if four_over_six else _lib().nvfp4_kv_quant
+    _check(fn(_ptr(kv), f, t, h, d, frame_block, ctypes.byref(ct), _ptr(ws), ws.numel() * 4, _stream(stream)),
+           "nvfp4_kv_quant_4over6" if four_over_six else "nvfp4_kv_quant")
     return out
 
 

@@ -185,8 +185,9 @@ int nvfp4_gemm_tiled(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int 
   return gemm_impl(a, b, c, c_dtype, ldc, epilogue, amax_out, tile_fa, tile_fb, stream);
 }
 
-int nvfp4_kv_quant(const void* kv, int64_t frames, int64_t tokens, int64_t heads, int64_t head_dim,
-                   int64_t frame_block, const nvfp4_tensor* out, void* ws, size_t ws_bytes, void* stream) {
+static int kv_quant_impl(const void* kv, int64_t frames, int64_t tokens, int64_t heads, int64_t head_dim,
+                         int64_t frame_block, const nvfp4_tensor* out, void* ws, size_t ws_bytes, void* stream,
+                         bool four_over_six) {
   if (!kv || !aligned16(kv) || frames < 0 || tokens < 0 || heads < 0 || head_dim < 0 || head_dim % 16 != 0 ||
       frame_block <= 0)
     return NVFP4_EINVAL;
@@ -204,7 +205,17 @@ int nvfp4_kv_quant(const void* kv, int64_t frames, int64_t tokens, int64_t heads
       hipSuccess)
     return NVFP4_EHIP;
   return from_hip(nvfp4::launch_encode_rows(kv, NVFP4_BF16, rows, head_dim, head_dim, rpd, parts, np,
-                                            qout(out), false, 0, s));
+                                            qout(out), false, 0, s, four_over_six));
+}
+
+int nvfp4_kv_quant(const void* kv, int64_t frames, int64_t tokens, int64_t heads, int64_t head_dim,
+                   int64_t frame_block, const nvfp4_tensor* out, void* ws, size_t ws_bytes, void* stream) {
+  return kv_quant_impl(kv, frames, tokens, heads, head_dim, frame_block, out, ws, ws_bytes, stream, false);
+}
+
+int nvfp4_kv_quant_4over6(const void* kv, int64_t frames, int64_t tokens, int64_t heads, int64_t head_dim,
+                          int64_t frame_block, const nvfp4_tensor* out, void* ws, size_t ws_bytes, void* stream) {
+  return kv_quant_impl(kv, frames, tokens, heads, head_dim, frame_block, out, ws, ws_bytes, stream, true);
 }
 
 int nvfp4_kv_dequant(const nvfp4_tensor* in, int64_t frames, int64_t tokens, int64_t heads, int64_t head_dim,

@@ -103,7 +103,13 @@ __global__ __launch_bounds__(kThreads) void amax_rows_kernel(
 // global block gi = d * rpd * bpr + i: elements [16 * (gi % bpr), +16) of row
 // gi / bpr; its codes are bytes [8 gi, 8 gi + 8) and its scale is byte gi of
 // the contiguous outputs.  `parts` holds `nparts` partial maxima per domain.
-template <int DT, bool RHT>
+//
+// FO6: Four Over Six encoder (tailorednewshub.com, "Inferencia W4A4 NVFP4":
+// adaptive scale selection for the KV cache).  Each block is encoded twice,
+// with the scale mapping its maximum to 6 and to 4, and the candidate with
+// the strictly smaller squared decode error (block_sq_error) is stored;
+// ties keep the core recipe.
+template <int DT, bool RHT, bool FO6>
 __global__ __launch_bounds__(kThreads) void encode_rows_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, int64_t rpd,
     const float* __restrict__ parts, int nparts, uint8_t* __restrict__ codes,
@@ -128,8 +134,17 @@ __global__ __launch_bounds__(kThreads) void encode_rows_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(v[j]));
     float rcp;
-    const uint32_t sig = block_scale(a, S, rcp);
-    const u32x2_t w = encode16(v, rcp);
+    uint32_t sig = block_scale(a, S, rcp);
+    u32x2_t w = encode16(v, rcp);
+    if constexpr (FO6) {
+      float rcp4;
+      const uint32_t sig4 = block_scale<4>(a, S, rcp4);
+      const u32x2_t w4 = encode16(v, rcp4);
+      if (block_sq_error(v, w4, sig4, S) < block_sq_error(v, w, sig, S)) {
+        sig = sig4;
+        w = w4;
+      }
+    }
     const int64_t gi = gbase + i;
     __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(codes) + gi);
     scales[gi] = (uint8_t)sig;
@@ -405,15 +420,21 @@ hipError_t launch_amax_parts_cols(const void* x, int dt, int64_t rows, int64_t c
 
 hipError_t launch_encode_rows(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
                               int64_t rpd, const float* parts, uint32_t nparts, QOut out, bool rht,
-                              uint32_t mask, hipStream_t s) {
+                              uint32_t mask, hipStream_t s, bool four_over_six) {
   if (rpd <= 0 || rpd > rows) rpd = rows;
   const int64_t ndom = (rows + rpd - 1) / rpd;
   const dim3 grid(encode_grid(rpd * (cols / kBlock), ndom), (unsigned)ndom);
-#define NVFP4_ENC_ROWS(D, R)                                                                       \
-  encode_rows_kernel<D, R><<<grid, kThreads, 0, s>>>(x, rows, cols, ld, rpd, parts, (int)nparts,  \
-                                                     out.codes, out.scales, out.tscale, mask)
-  if (dt == 0) { if (rht) NVFP4_ENC_ROWS(0, true); else NVFP4_ENC_ROWS(0, false); }
-  else { if (rht) NVFP4_ENC_ROWS(1, true); else NVFP4_ENC_ROWS(1, false); }
+#define NVFP4_ENC_ROWS(D, R, F)                                                                       \
+  encode_rows_kernel<D, R, F><<<grid, kThreads, 0, s>>>(x, rows, cols, ld, rpd, parts, (int)nparts,  \
+                                                        out.codes, out.scales, out.tscale, mask)
+  if (four_over_six) {  // no RHT variant: the KV cache is quantized without it
+    if (rht) return hipErrorInvalidValue;
+    if (dt == 0) NVFP4_ENC_ROWS(0, false, true); else NVFP4_ENC_ROWS(1, false, true);
+  } else if (dt == 0) {
+    if (rht) NVFP4_ENC_ROWS(0, true, false); else NVFP4_ENC_ROWS(0, false, false);
+  } else {
+    if (rht) NVFP4_ENC_ROWS(1, true, false); else NVFP4_ENC_ROWS(1, false, false);
+  }
 #undef NVFP4_ENC_ROWS
   return hipGetLastError();
 }

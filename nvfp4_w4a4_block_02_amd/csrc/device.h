@@ -131,9 +131,12 @@ __device__ __forceinline__ void rht16(float (&v)[16], uint32_t mask) {
 
 // Scale part of the recipe for one block: given the block amax `a` and the
 // domain's tensor scale S, return the E4M3 byte and the element multiplier
-// r = 1 / (f32(s_b) * S) (0 when that product is 0).
+// r = 1 / (f32(s_b) * S) (0 when that product is 0).  TARGET is the E2M1
+// value the block maximum maps to: 6 in the core recipe, 4 for the second
+// candidate of Four Over Six.
+template <int TARGET = 6>
 __device__ __forceinline__ uint32_t block_scale(float a, float S, float& r) {
-  const float t = a / 6.0f;
+  const float t = a / (float)TARGET;
   const float u = S > 0.0f ? t / S : 0.0f;
   const uint32_t sig = e4m3_rne_satfinite(u);
   const float d = e4m3_to_f32(sig) * S;
@@ -155,6 +158,28 @@ __device__ __forceinline__ u32x2_t encode16(const float (&v)[16], float r) {
   w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[12] * r, v[13] * r, 1.0f, 2);
   w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[14] * r, v[15] * r, 1.0f, 3);
   return u32x2_t{w0, w1};
+}
+
+// Squared decode error of one encoded block (Four Over Six): with
+// x'_i = f32(e2m1_i * s_b) * S the standard decode, E = sum (x_i - x'_i)^2,
+// every operation a separately rounded float32 operation, summed from
+// element 0 to 15 — the exact order the CPU reference uses, because the
+// comparison of two such errors decides which bytes are stored.
+__device__ __forceinline__ void decode8_f32(uint32_t w, float* o);
+__device__ __forceinline__ float block_sq_error(const float (&v)[16], u32x2_t codes, uint32_t sig, float S) {
+#pragma clang fp contract(off)
+  float e2[16];
+  decode8_f32(codes.x, e2);
+  decode8_f32(codes.y, e2 + 8);
+  const float sf = e4m3_to_f32(sig);
+  float E = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float xd = (e2[i] * sf) * S;
+    const float d = v[i] - xd;
+    E = E + d * d;
+  }
+  return E;
 }
 
 // Decode 8 packed E2M1 codes (one dword, low nibble first) to float32.

@@ -38,9 +38,10 @@ hipError_t launch_amax_parts_cols(const void* x, int dt, int64_t rows, int64_t c
 hipError_t launch_reduce_parts(const float* parts, uint32_t nparts, int64_t ndom, float* amax, hipStream_t s);
 
 // Steps 2-6 from per-domain partial maxima (nparts = 1: final amax values).
+// four_over_six: Four Over Six block-scale selection (not combined with rht).
 hipError_t launch_encode_rows(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
                               int64_t rows_per_domain, const float* parts, uint32_t nparts, QOut out,
-                              bool rht, uint32_t mask, hipStream_t s);
+                              bool rht, uint32_t mask, hipStream_t s, bool four_over_six = false);
 hipError_t launch_encode_cols(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
                               const float* parts, uint32_t nparts, QOut out, bool rht, uint32_t mask,
                               hipStream_t s);

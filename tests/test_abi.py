@@ -125,14 +125,19 @@ def test_gemm_rejects_bad_arguments(nv):
     assert gt(ctypes.byref(_t(nv, 0, 64)), ctypes.byref(b), c, 0, 16, 0, None, 4, 4, _stream()) == 0
 
 
-def test_kv_rejects_bad_arguments(nv):
-    kq = nv.lib.nvfp4_kv_quant
+@pytest.mark.parametrize("entry", ["nvfp4_kv_quant", "nvfp4_kv_quant_4over6"])
+def test_kv_rejects_bad_arguments(nv, entry):
+    kq = getattr(nv.lib, entry)
     out = _t(nv, 12 * 4 * 2, 32)
     ws = ctypes.c_void_p(FAKE)
-    assert kq(ctypes.c_void_p(FAKE), 12, 4, 2, 32, 0, ctypes.byref(out), ws, 4096, _stream()) == -1  # frame_block
-    assert kq(ctypes.c_void_p(FAKE), 12, 4, 2, 24, 8, ctypes.byref(_t(nv, 96, 24)), ws, 4096, _stream()) == -1
-    assert kq(ctypes.c_void_p(FAKE), 12, 4, 2, 32, 8, ctypes.byref(_t(nv, 95, 32)), ws, 4096, _stream()) == -1
+    assert kq(ctypes.c_void_p(FAKE), 12, 4, 2, 32, 0, ctypes.byref(out), ws, 8192, _stream()) == -1  # frame_block
+    assert kq(ctypes.c_void_p(FAKE), 12, 4, 2, 24, 8, ctypes.byref(_t(nv, 96, 24)), ws, 8192, _stream()) == -1
+    assert kq(ctypes.c_void_p(FAKE), 12, 4, 2, 32, 8, ctypes.byref(_t(nv, 95, 32)), ws, 8192, _stream()) == -1
+    assert kq(None, 12, 4, 2, 32, 8, ctypes.byref(out), ws, 8192, _stream()) == -1
+    assert kq(ctypes.c_void_p(FAKE), 12, 4, 2, 32, 8, ctypes.byref(out), None, 8192, _stream()) == -1
+    assert kq(ctypes.c_void_p(FAKE), 12, 4, 2, 32, 8, ctypes.byref(out), ws, 4096, _stream()) == -3  # 2 domains
     assert kq(ctypes.c_void_p(FAKE), 40, 4, 2, 32, 8, ctypes.byref(_t(nv, 320, 32)), ws, 4096, _stream()) == -3
+    assert kq(ctypes.c_void_p(FAKE), 0, 4, 2, 32, 8, ctypes.byref(_t(nv, 0, 32)), ws, 4096, _stream()) == 0
     kd = nv.lib.nvfp4_kv_dequant
     assert kd(ctypes.byref(out), 12, 4, 2, 32, 8, None, _stream()) == -1
     assert kd(ctypes.byref(out), 12, 4, 2, 32, 8, ctypes.c_void_p(FAKE + 8), _stream()) == -1

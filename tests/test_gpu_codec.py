@@ -182,6 +182,34 @@ def test_kv_codec_small(nv, shape):
     assert np.array_equal(y, oracle.kv_dequantize(oq, f, t, h, d))
 
 
+@pytest.mark.parametrize("shape", [(12, 5, 3, 32), (9, 7, 2, 128), (17, 2, 1, 16), (3, 40, 4, 64)])
+def test_kv_codec_four_over_six(nv, shape):
+    f, t, h, d = shape
+    log(f"kv codec Four Over Six {shape}")
+    kv = workloads.kv_cache(frames=f, tokens=t, heads=h, head_dim=d, seed=90 + f)["v"]
+    gq = nv.kv_quant(dev_bf16(kv), four_over_six=True)
+    oq = oracle.kv_quantize_4over6(widen(kv))
+    torch.cuda.synchronize()
+    assert_q_exact(gq, oq, f"kv 4/6 {shape}")
+    y = host_bf16_bits(nv.kv_dequant(gq, shape))
+    assert np.array_equal(y, oracle.kv_dequantize(oq, f, t, h, d))
+
+
+def test_four_over_six_hand_worked_blocks_on_gpu(nv, golden_dir):
+    """The hand-worked Four Over Six blocks (tests/golden) through the KV
+    entry point as one frame of one token and one head (head_dim 80)."""
+    with open(os.path.join(golden_dir, "four_over_six_blocks.json")) as fh:
+        g = json.load(fh)
+    x = np.array(g["x"], np.float32)
+    bits = host_bf16_bits(torch.from_numpy(x).to(torch.bfloat16))
+    assert np.array_equal(widen(bits), x)  # every value is exact in bf16
+    gq = nv.kv_quant(dev_bf16(bits.reshape(1, 1, 1, -1)), four_over_six=True)
+    torch.cuda.synchronize()
+    assert gq.tscale.cpu().numpy()[0] == np.float32(g["tscale"])
+    assert [f"{b:02X}" for b in gq.scales.cpu().numpy()[0]] == g["scales"]
+    assert [f"{b:02X}" for b in gq.codes.cpu().numpy()[0]] == g["codes_hex"]
+
+
 @pytest.mark.parametrize("rows,cols", [(16, 16), (64, 48), (255, 512), (48, 1040)])
 @pytest.mark.parametrize("axis", [1, 0])
 def test_rht16_quantize_matches_oracle(nv, rows, cols, axis):
@@ -222,6 +250,19 @@ def test_full_kv_codec(nv):
         oq = oracle.kv_quantize(widen(d[name]).reshape(shape))
         torch.cuda.synchronize()
         assert_q_exact(gq, oq, f"kv {name}")
+        y = host_bf16_bits(nv.kv_dequant(gq, shape))
+        assert np.array_equal(y, oracle.kv_dequantize(oq, *shape))
+
+
+def test_full_kv_codec_four_over_six(nv):
+    d = workloads.kv_cache()
+    shape = (12, 880, 24, 128)
+    for name in ("k", "v"):
+        log(f"full-size KV codec, Four Over Six, {name} {shape}")
+        gq = nv.kv_quant(dev_bf16(d[name]), four_over_six=True)
+        oq = oracle.kv_quantize_4over6(widen(d[name]).reshape(shape))
+        torch.cuda.synchronize()
+        assert_q_exact(gq, oq, f"kv 4/6 {name}")
         y = host_bf16_bits(nv.kv_dequant(gq, shape))
         assert np.array_equal(y, oracle.kv_dequantize(oq, *shape))
 
