@@ -66,9 +66,15 @@ __device__ __forceinline__ half2_t scale_h2(uint32_t sw, int q) {
   return half2_t{v, v};
 }
 
+// GELU, tanh form: g(h) = 0.5 h (1 + tanh(u)), u = sqrt(2/pi) (h + 0.044715 h^3).
+// Evaluated through the identity 0.5 (1 + tanh(u)) = 1 / (1 + e^(-2u)) as
+// g = h / (1 + 2^(-2u log2 e)) with the hardware exp2 and reciprocal: a few
+// float32 ulp, no cancellation in either tail (g -> h for large h, g -> -0
+// for large negative h, where 2^(...) overflows to +inf and 1/inf = 0).
 __device__ __forceinline__ float gelu_tanh(float h) {
-  const float c = 0.7978845608028654f;  // sqrt(2 / pi)
-  return 0.5f * h * (1.0f + tanhf(c * (h + 0.044715f * h * h * h)));
+  const float k = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  const float w = k * (h + 0.044715f * (h * h * h));
+  return h * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(w));
 }
 
 // One K-tile of this lane's fragments: 32 code bytes and 4 scale bytes each.
