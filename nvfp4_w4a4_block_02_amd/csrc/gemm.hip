@@ -34,6 +34,8 @@
 //
 // Fallback kernel (any K % 16 == 0): the same fragments loaded straight into
 // registers with bounds checks; code bytes past K read as 0.
+#include <cmath>
+
 #include "device.h"
 #include "internal.h"
 
@@ -168,16 +170,32 @@ __device__ __forceinline__ void store_tile(const float16_t (&acc)[FA][FB], float
   }
 }
 
-// Workgroup -> output tile.  Workgroups are dealt round-robin to the 8 XCDs
-// (each with its own L2); renumber so that XCD x works on a contiguous range
-// of tiles in row-major order, which keeps the A rows and B columns an XCD
-// touches together.
-__device__ __forceinline__ void tile_of(int tiles_n, int ntiles, int& tm, int& tn) {
+// Workgroup -> output tile.  Workgroups are dealt round-robin to the 8 XCDs,
+// each with its own L2.  Tiles are put in "band" order (bands of `band` tile
+// columns, row-major inside a band) and every XCD gets one contiguous run of
+// that order, so the ~32 tiles an XCD runs at once form a compact block of
+// A rows and B columns that its L2 can hold; `band` is chosen on the host to
+// make that block roughly square in bytes.  A bijection for any tile count.
+__device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int band, int& tm, int& tn) {
+  const int ntiles = tiles_m * tiles_n;
   const int id = blockIdx.x;
-  int t = id;
-  if (ntiles % 8 == 0) t = (id % 8) * (ntiles / 8) + id / 8;
-  tm = t / tiles_n;
-  tn = t - tm * tiles_n;
+  const int x = id % 8, local = id / 8, q = ntiles / 8, r = ntiles % 8;
+  const int t = x * q + (x < r ? x : r) + local;  // position in band order
+  const int full = tiles_n / band;                 // bands of full width
+  const int per_band = band * tiles_m;
+  const int b = t / per_band;
+  int n0, w, loc;
+  if (b < full) {
+    n0 = b * band;
+    w = band;
+    loc = t - b * per_band;
+  } else {  // the last, narrower band
+    n0 = full * band;
+    w = tiles_n - n0;
+    loc = t - full * per_band;
+  }
+  tm = loc / w;
+  tn = n0 + (loc - tm * w);
 }
 
 // ---------------------------------------------------------------------------
@@ -244,7 +262,7 @@ template <int FA, int FB, int OUT, int EPI>
 __global__ __launch_bounds__(256) void gemm_lds_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts,
-    void* __restrict__ c, int64_t ldc, int M, int N, int K, float* __restrict__ amax_out) {
+    void* __restrict__ c, int64_t ldc, int M, int N, int K, float* __restrict__ amax_out, int band) {
   constexpr int NFA = 2 * FA, NFB = 2 * FB;                  // fragments per workgroup
   constexpr int OFF_B = NFA * 2048, OFF_SA = OFF_B + NFB * 2048, OFF_SB = OFF_SA + NFA * 256;
   constexpr int STAGE = OFF_SB + NFB * 256;
@@ -261,7 +279,7 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
   const int tiles_n = (N + 64 * FB - 1) / (64 * FB);
   const int tiles_m = (M + 64 * FA - 1) / (64 * FA);
   int tm, tn;
-  tile_of(tiles_n, tiles_m * tiles_n, tm, tn);
+  tile_of(tiles_m, tiles_n, band, tm, tn);
   const int mwg = tm * 64 * FA, nwg = tn * 64 * FB;
   const int64_t cpitch = K / 2, spitch = K / 16;
 
@@ -435,11 +453,25 @@ struct Args {
   float* amax;
 };
 
+// Band width for tile_of: the ~32 tiles one XCD runs at once (32 CUs) span
+// about sqrt(32 tileM / tileN) band columns, which balances the A and B
+// bytes they touch.
+inline int band_for(int tiles_m, int tiles_n, int tile_m, int tile_n) {
+  const int ntiles = tiles_m * tiles_n;
+  int conc = (ntiles + 7) / 8;
+  if (conc > 32) conc = 32;
+  int w = (int)std::lround(std::sqrt((double)conc * tile_m / tile_n));
+  if (w < 1) w = 1;
+  if (w > tiles_n) w = tiles_n;
+  return w;
+}
+
 template <int FA, int FB, int OUT, int EPI>
 void launch_lds(const Args& g, hipStream_t s) {
-  const int tiles = ((g.m + 64 * FA - 1) / (64 * FA)) * ((g.n + 64 * FB - 1) / (64 * FB));
-  gemm_lds_kernel<FA, FB, OUT, EPI><<<tiles, 256, 0, s>>>(g.a.codes, g.a.scales, g.a.tscale, g.b.codes, g.b.scales,
-                                                          g.b.tscale, g.c, g.ldc, g.m, g.n, g.k, g.amax);
+  const int tiles_m = (g.m + 64 * FA - 1) / (64 * FA), tiles_n = (g.n + 64 * FB - 1) / (64 * FB);
+  const int band = band_for(tiles_m, tiles_n, 64 * FA, 64 * FB);
+  gemm_lds_kernel<FA, FB, OUT, EPI><<<tiles_m * tiles_n, 256, 0, s>>>(
+      g.a.codes, g.a.scales, g.a.tscale, g.b.codes, g.b.scales, g.b.tscale, g.c, g.ldc, g.m, g.n, g.k, g.amax, band);
 }
 
 template <int OUT, int EPI>
