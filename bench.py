@@ -8,14 +8,20 @@ activations, their NVFP4 encode, and the block-scaled W4A4 GEMM against
 pre-quantized 3072x3072 NVFP4 weights into bf16.  The timed region starts
 with every input resident in HBM; buffers rotate over 13 independent sets
 (> 512 MB) so the 256 MB Infinity Cache cannot serve a step from the last
-one.  Prints ONE JSON line.
+one.  The timed steps run back to back with nothing between them (a HIP
+event recorded between two kernels idles the GPU for ~10 us on this part, so
+per-kernel events would distort the step time); per-kernel durations come
+from separate back-to-back passes over the same buffers, each timed by one
+pair of HIP events on the launch stream.  Prints ONE JSON line.
 
 Besides the headline value the line carries:
-  roofline      the GEMM kernel (the dominant kernel), timed with HIP events
-                on its own stream inside the timed region;
+  roofline      the GEMM kernel (the dominant kernel): its algorithmic
+                flops per launch / its mean duration over back-to-back
+                launches on the launch stream;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same
                 workload on this host;
-  rows          the other rows of the path, each timed the same way: KV codec
+  rows          the other rows of the path, each timed back to back the same
+                way: KV codec
                 quantize (core recipe and Four Over Six) and dequantize
                 (12x880x24x128 bf16, K and V), RHT16 +
                 quantize of a 16384x3072 gradient along dim 0, the 3072x3072x
@@ -51,27 +57,34 @@ def _args():
     p.add_argument("--no-rows", action="store_true", help="skip the per-row extra measurements")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--sets", type=int, default=13, help="rotating buffer sets")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run three 256 MiB device-to-device copies (calibrates the rocprofv3 "
+                        "FETCH_SIZE / WRITE_SIZE counters against a known byte count) and exit")
     return p.parse_args()
 
 
-class Timer:
-    """Pairs of HIP events recorded on one stream around one kernel call."""
+def copy_probe():
+    import torch
 
-    def __init__(self, torch, stream, n):
-        self.torch = torch
-        self.stream = stream
-        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        self.i = 0
+    x = torch.ones(1 << 26, device="cuda")  # 256 MiB of float32
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": x.numel() * 4, "copies": 3}), flush=True)
 
-    def start(self):
-        self.ev[self.i][0].record(self.stream)
 
-    def stop(self):
-        self.ev[self.i][1].record(self.stream)
-        self.i += 1
-
-    def mean_ms(self):
-        return float(np.mean([a.elapsed_time(b) for a, b in self.ev[: self.i]]))
+def _b2b_ms(torch, stream, fn, n):
+    """Mean duration of `n` back-to-back calls of `fn(i)` on `stream`, from
+    one pair of HIP events around all of them (events between the calls would
+    stall the queue and add their own gaps)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
 
 
 def _profiled_traffic():
@@ -111,58 +124,47 @@ def bench_attn_proj(nv, torch, wl, steps, warmup, nsets):
             "y": torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
         })
     stream = torch.cuda.current_stream()
-    tq = Timer(torch, stream, steps)
-    tg = Timer(torch, stream, steps)
 
-    def step(s, timed):
-        if timed:
-            tq.start()
+    def step(s):
         nv.quantize(s["x"], out=s["xq"], ws=s["ws"], stream=stream)
-        if timed:
-            tq.stop()
-            tg.start()
         nv.gemm(s["xq"], s["wq"], out=s["y"], stream=stream)
-        if timed:
-            tg.stop()
 
     for i in range(warmup):
-        step(sets[i % nsets], False)
+        step(sets[i % nsets])
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(sets[i % nsets], True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # GEMM kernel duration for the roofline: back-to-back launches on the same
-    # stream between one event pair (per-launch events would add the dispatch
-    # gap after the preceding quantize kernel to every sample).
+    # The timed region: `steps` steps back to back, nothing else on the
+    # stream; wall clock, and one event pair on the stream as a cross-check.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
     e0.record(stream)
     for i in range(steps):
-        s = sets[i % nsets]
-        nv.gemm(s["xq"], s["wq"], out=s["y"], stream=stream)
+        step(sets[i % nsets])
     e1.record(stream)
     torch.cuda.synchronize()
-    gemm_b2b_ms = e0.elapsed_time(e1) / steps
+    wall = time.perf_counter() - t0
+    step_event_ms = e0.elapsed_time(e1) / steps
+    # Per-kernel durations, from back-to-back passes over the same rotating
+    # buffer sets: the activation quantize (amax + encode) and the GEMM.
+    quant_ms = _b2b_ms(torch, stream, lambda i: nv.quantize(sets[i % nsets]["x"], out=sets[i % nsets]["xq"],
+                                                           ws=sets[i % nsets]["ws"], stream=stream), steps)
+    gemm_b2b_ms = _b2b_ms(torch, stream, lambda i: nv.gemm(sets[i % nsets]["xq"], sets[i % nsets]["wq"],
+                                                          out=sets[i % nsets]["y"], stream=stream), steps)
     flops = 2.0 * m * n * k
     quant_bytes = m * k * 2 + m * k // 2 + m * k // 16 + 4
     return {
-        "m": m, "n": n, "k": k, "wall_s": wall, "ms_per_step": wall * 1e3 / steps,
-        "gemm_ms": gemm_b2b_ms, "gemm_in_step_ms": tg.mean_ms(), "quant_ms": tq.mean_ms(), "flops": flops,
-        "quant_bytes": quant_bytes,
+        "m": m, "n": n, "k": k, "wall_s": wall, "ms_per_step": wall * 1e3 / steps, "step_event_ms": step_event_ms,
+        "gemm_ms": gemm_b2b_ms, "quant_ms": quant_ms, "flops": flops, "quant_bytes": quant_bytes,
     }
 
 
 def _time_loop(torch, fn, sets, steps, warmup):
+    """Mean time of one call of `fn(set)` over `steps` back-to-back calls that
+    rotate through `sets` (after `warmup` untimed calls)."""
     stream = torch.cuda.current_stream()
-    t = Timer(torch, stream, steps)
     for i in range(warmup):
-        fn(sets[i % len(sets)], None)
+        fn(sets[i % len(sets)])
     torch.cuda.synchronize()
-    for i in range(steps):
-        fn(sets[i % len(sets)], t)
-    torch.cuda.synchronize()
-    return t.mean_ms()
+    return _b2b_ms(torch, stream, lambda i: fn(sets[i % len(sets)]), steps)
 
 
 def bench_rows(nv, torch, wl, steps, warmup):
@@ -181,23 +183,17 @@ def bench_rows(nv, torch, wl, steps, warmup):
         s["ws"] = nv._workspace(nv.OP_KV_QUANT, 12, 8, "cuda")
         kvsets.append(s)
 
-    def kvq(s, t):
-        if t: t.start()
+    def kvq(s):
         nv.kv_quant(s["k"], out=s["kq"], ws=s["ws"], stream=stream)
         nv.kv_quant(s["v"], out=s["vq"], ws=s["ws"], stream=stream)
-        if t: t.stop()
 
-    def kvq6(s, t):
-        if t: t.start()
+    def kvq6(s):
         nv.kv_quant(s["k"], out=s["kq"], ws=s["ws"], stream=stream, four_over_six=True)
         nv.kv_quant(s["v"], out=s["vq"], ws=s["ws"], stream=stream, four_over_six=True)
-        if t: t.stop()
 
-    def kvd(s, t):
-        if t: t.start()
+    def kvd(s):
         nv.kv_dequant(s["kq"], shape, out=s["ko"], stream=stream)
         nv.kv_dequant(s["vq"], shape, out=s["vo"], stream=stream)
-        if t: t.stop()
 
     elems = 2 * 12 * 880 * 24 * 128
     kv_bytes = elems * 2 + elems // 2 + elems // 16 + 2 * 2 * 4
@@ -222,15 +218,11 @@ def bench_rows(nv, torch, wl, steps, warmup):
         s["c"] = torch.empty((cols, cols), dtype=torch.float32, device="cuda")
         rsets.append(s)
 
-    def rq(s, t):
-        if t: t.start()
+    def rq(s):
         nv.rht16_quantize(s["g"], d["mask"], axis=0, out=s["gq"], ws=s["ws"], stream=stream)
-        if t: t.stop()
 
-    def wg(s, t):
-        if t: t.start()
+    def wg(s):
         nv.gemm(s["gq"], s["xq"], out=s["c"], stream=stream)
-        if t: t.stop()
 
     rbytes = rows * cols * 2 + rows * cols // 2 + rows * cols // 16 + 4
     ms = _time_loop(torch, rq, rsets, steps, warmup)
@@ -252,10 +244,8 @@ def bench_rows(nv, torch, wl, steps, warmup):
             "hmax": torch.empty(1, device="cuda"), "hq": nv.NVFP4Tensor.empty(m, f, 1, "cuda"),
             "y": torch.empty((m, dm), dtype=torch.bfloat16, device="cuda")}
 
-    def ffn(s, t):
-        if t: t.start()
+    def ffn(s):
         nv.ffn(x, w1, w2, bufs=bufs, stream=stream)
-        if t: t.stop()
 
     ms = _time_loop(torch, ffn, [None], max(steps // 5, 3), 2)
     fl = 2.0 * m * dm * f * 2
@@ -295,6 +285,9 @@ def cpu_baseline(wl):
 
 def main():
     a = _args()
+    if a.copy_probe:
+        copy_probe()
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {a.gpus} is not supported by this build "
               "(the NVFP4 path here has no multi-GPU component)", file=sys.stderr)
@@ -315,6 +308,7 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": round(r["ms_per_step"], 5),
+        "ms_per_step_events": round(r["step_event_ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -326,7 +320,6 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(gemm_tf, 2), "peak": PEAK_TFLOPS["f16"],
                      "unit": "TFLOP/s", "frac": round(gemm_tf / PEAK_TFLOPS["f16"], 4), "traffic": _profiled_traffic(),
                      "kernel": "gemm_lds_kernel (nvfp4_gemm)", "kernel_ms": round(r["gemm_ms"], 5),
-                     "kernel_ms_in_step": round(r["gemm_in_step_ms"], 5),
                      "frac_fp8_peak": round(gemm_tf / PEAK_TFLOPS["fp8"], 4),
                      "frac_fp4_peak": round(gemm_tf / PEAK_TFLOPS["fp4"], 4)},
         "act_quant": {"ms": round(r["quant_ms"], 5), "GB/s": round(r["quant_bytes"] / r["quant_ms"] / 1e6, 1),
