@@ -67,6 +67,7 @@ from .codec import (  # noqa: F401
 )
 from .rht import hadamard16, sign_vector, rht16_rows, rht16_quantize  # noqa: F401
 from .gemm import gemm_ref, gelu_tanh, ffn_chain  # noqa: F401
+from .train import linear_train_ref  # noqa: F401
 from .four_over_six import (  # noqa: F401
     block_scales_to,
     block_sq_error,

@@ -13,6 +13,11 @@ heads of 128, a KV window of 3 sink + 9 local latent frames (171host.com
 with the stated distributions stand in for activations, weights, gradients
 and KV.
 
+Workload 6 is not one of the five quoted configurations: it is the
+training slice of one linear layer (forward, input gradient, weight
+gradient) at the attention-projection shape, the input of the NVFP4
+training GEMM triple.
+
 Seeds: data ``1000 + workload number``, RHT sign mask ``2000 + workload
 number``; robustness reruns add 100 or 200 to the data seed.  bf16 tensors are
 returned as uint16 bit patterns (round-to-nearest-even cast done by torch on
@@ -29,6 +34,7 @@ WORKLOADS = {
     3: "dit_ffn_10560x3072x14336",
     4: "kv_codec_12x880x24x128",
     5: "rht_wgrad_16384x3072",
+    6: "train_linear_2640x3072x3072",
 }
 
 
@@ -97,3 +103,18 @@ def rht_wgrad(rows=16384, cols=3072, seed=1005, mask_seed=2005):
     x = rng.standard_normal((rows, cols), dtype=np.float32)
     mask = int(np.random.default_rng(mask_seed).integers(0, 2 ** 16))
     return {"g": to_bf16_bits(g), "x": to_bf16_bits(x), "mask": mask}
+
+
+def train_linear(m=2640, n=3072, k=3072, seed=1006, mask_seed=2006):
+    """Workload 6: one linear layer Y = X W^T in training at the attention-
+    projection shape: X bf16 [m, k] as in workload 2, master weight W fp32
+    [n, k] ~ N(0, 0.02^2), output gradient dY bf16 [m, n] ~ Laplace(0, 1e-3)
+    with 0.1% of entries x100 (as the gradient of workload 5), and the RHT sign
+    mask of the weight-gradient operands."""
+    rng = np.random.default_rng(seed)
+    c = np.exp(rng.uniform(np.log(0.1), np.log(10.0), size=k)).astype(np.float32)
+    x = rng.standard_normal((m, k), dtype=np.float32) * c[None, :]
+    w = (rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)).astype(np.float32)
+    dy = _outliers(rng, rng.laplace(0.0, 1e-3, size=(m, n)).astype(np.float32), 0.001, 100.0)
+    mask = int(np.random.default_rng(mask_seed).integers(0, 2 ** 16))
+    return {"x": to_bf16_bits(x), "w": w, "dy": to_bf16_bits(dy), "mask": mask}
