@@ -25,8 +25,10 @@ Besides the headline value the line carries:
                 quantize (core recipe and Four Over Six) and dequantize
                 (12x880x24x128 bf16, K and V), RHT16 +
                 quantize of a 16384x3072 gradient along dim 0, the 3072x3072x
-                16384 weight-gradient GEMM, and the FFN pair
-                (10560x3072 -> 14336 -> 3072).
+                16384 weight-gradient GEMM, the FFN pair
+                (10560x3072 -> 14336 -> 3072), and the NVFP4 training triple
+                (forward, input and weight gradient, with the six operand
+                quantizations) of a 2640x3072x3072 linear layer.
 """
 
 from __future__ import annotations
@@ -250,6 +252,31 @@ def bench_rows(nv, torch, wl, steps, warmup):
     ms = _time_loop(torch, ffn, [None], max(steps // 5, 3), 2)
     fl = 2.0 * m * dm * f * 2
     out["ffn_pair"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_f16_peak": fl / ms / 1e9 / PEAK_TFLOPS["f16"]}
+    del bufs, x, w1, w2
+    # Training triple of one linear layer at the attention-projection shape:
+    # six quantizations (two with the RHT16) and three GEMMs per step.
+    d = wl.train_linear()
+    m, k = d["x"].shape
+    n = d["w"].shape[0]
+    tsets = []
+    for i in range(3):
+        s = {"x": _dev_bf16(torch, d["x"]), "w": torch.from_numpy(d["w"]).cuda(), "dy": _dev_bf16(torch, d["dy"])}
+        s["bufs"] = {"xq": nv.NVFP4Tensor.empty(m, k, 1, "cuda"), "wq": nv.NVFP4Tensor.empty(n, k, 1, "cuda"),
+                     "dyq": nv.NVFP4Tensor.empty(m, n, 1, "cuda"), "wtq": nv.NVFP4Tensor.empty(k, n, 1, "cuda"),
+                     "dyt": nv.NVFP4Tensor.empty(n, -(-m // 128) * 128, 1, "cuda"),
+                     "xt": nv.NVFP4Tensor.empty(k, -(-m // 128) * 128, 1, "cuda"),
+                     "y": torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
+                     "dx": torch.empty((m, k), dtype=torch.bfloat16, device="cuda"),
+                     "dw": torch.empty((n, k), dtype=torch.float32, device="cuda"),
+                     "ws": nv._workspace(nv.OP_RHT16, m, max(k, n), "cuda")}
+        tsets.append(s)
+
+    def train(s):
+        nv.linear_train(s["x"], s["w"], s["dy"], d["mask"], bufs=s["bufs"], stream=stream)
+
+    ms = _time_loop(torch, train, tsets, max(steps // 2, 5), 2)
+    fl = 3 * 2.0 * m * n * k
+    out["train_linear_triple"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_f16_peak": fl / ms / 1e9 / PEAK_TFLOPS["f16"]}
     return out
 
 

@@ -123,10 +123,14 @@ int nvfp4_amax(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
  *   axis = 1: blocks run along cols (x is [rows][cols], K-contiguous); the
  *             output is rows x cols.
  *   axis = 0: blocks run along rows (x's reduction dim is dim 0, as for a
- *             weight gradient); the output is stored transposed, cols x rows,
- *             and rows_per_domain must be 0.
- * `out` must describe the output shape exactly; out->tscale needs one float
- * per domain.
+ *             weight gradient); the output is stored transposed, cols x
+ *             out->k, and rows_per_domain must be 0.  out->k may exceed rows
+ *             (a multiple of 16): the blocks past rows get zero codes and
+ *             zero scales, which decode to 0 and leave a GEMM over the padded
+ *             reduction dimension unchanged (nvfp4_gemm runs its fastest path
+ *             when K % 64 == 0).
+ * `out` must describe the output shape exactly (for axis 1: rows x cols);
+ * out->tscale needs one float per domain.
  */
 int nvfp4_encode(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                  int axis, int64_t rows_per_domain, const float *amax,

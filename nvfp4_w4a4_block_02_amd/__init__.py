@@ -208,11 +208,13 @@ def quantize(x: torch.Tensor, axis: int = 1, out: NVFP4Tensor | None = None, ws:
 
 
 def rht16_quantize(x: torch.Tensor, sign_mask: int, axis: int = 1, out: NVFP4Tensor | None = None,
-                   ws: torch.Tensor | None = None, stream=None) -> NVFP4Tensor:
+                   ws: torch.Tensor | None = None, stream=None, k_pad: int = 0) -> NVFP4Tensor:
+    """RHT16 then quantize; for axis 0, ``k_pad`` > rows zero-pads the output's
+    reduction dimension to that length (zero codes and scales)."""
     rows, cols = x.shape
     if out is None:
         r, k = _out_shape(x, axis)
-        out = NVFP4Tensor.empty(r, k, 1, x.device)
+        out = NVFP4Tensor.empty(r, max(k, k_pad) if axis == 0 else k, 1, x.device)
     if ws is None:
         ws = _workspace(OP_RHT16, rows, cols, x.device)
     ct = out.c()
@@ -306,3 +308,33 @@ def ffn(x: torch.Tensor, w1: NVFP4Tensor, w2: NVFP4Tensor, out_dtype=torch.bfloa
     gemm(xq, w1, epilogue=EPI_GELU_TANH, amax_out=hmax, out=h, stream=stream)
     hq = encode(h, hmax, out=bufs.get("hq"), stream=stream)
     return gemm(hq, w2, out_dtype=out_dtype, out=bufs.get("y"), stream=stream)
+
+
+def linear_train(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, sign_mask: int, bufs: dict | None = None,
+                 stream=None):
+    """The NVFP4 GEMM triple of one linear layer Y = X W^T in training; each
+    GEMM quantizes both operands along its own reduction dimension, and the
+    weight-gradient operands go through the RHT16 first (one sign mask for
+    both):
+
+      y  = Q(X) Q(W)^T          (bf16)   x [M, K], w [N, K] (master weight)
+      dx = Q(dY) Q(W^T)^T       (bf16)   dy [M, N]; W quantized along dim 0
+      dw = R(dY^T) R(X^T)^T     (f32)    dY and X quantized along dim 0
+
+    Returns (y, dx, dw).  Only sequences C-ABI calls.  Preallocated ``bufs``
+    must give "dyt" / "xt" a K of M rounded up to 128."""
+    b = bufs if bufs is not None else {}
+    xq = quantize(x, axis=1, out=b.get("xq"), ws=b.get("ws"), stream=stream)
+    wq = quantize(w, axis=1, out=b.get("wq"), ws=b.get("ws"), stream=stream)
+    y = gemm(xq, wq, out_dtype=torch.bfloat16, out=b.get("y"), stream=stream)
+    dyq = quantize(dy, axis=1, out=b.get("dyq"), ws=b.get("ws"), stream=stream)
+    wtq = quantize(w, axis=0, out=b.get("wtq"), ws=b.get("ws"), stream=stream)
+    dx = gemm(dyq, wtq, out_dtype=torch.bfloat16, out=b.get("dx"), stream=stream)
+    # The weight gradient reduces over M; its operands are zero-padded to a
+    # multiple of 128 along M (exact: zero blocks add nothing) so that the
+    # GEMM runs its pipelined path for any token count.
+    mp = -(-x.shape[0] // 128) * 128
+    dyt = rht16_quantize(dy, sign_mask, axis=0, out=b.get("dyt"), ws=b.get("ws"), stream=stream, k_pad=mp)
+    xt = rht16_quantize(x, sign_mask, axis=0, out=b.get("xt"), ws=b.get("ws"), stream=stream, k_pad=mp)
+    dw = gemm(dyt, xt, out_dtype=torch.float32, out=b.get("dw"), stream=stream)
+    return y, dx, dw

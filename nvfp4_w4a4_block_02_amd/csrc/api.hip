@@ -44,11 +44,13 @@ int check_dense_to_q(const void* x, int dt, int64_t rows, int64_t cols, int64_t 
   if (axis == 1) {
     if (cols % 16 != 0 || out->rows != rows || out->k != cols) return NVFP4_EINVAL;
   } else if (axis == 0) {
-    if (rows % 16 != 0 || out->rows != cols || out->k != rows) return NVFP4_EINVAL;
+    if (rows % 16 != 0 || out->rows != cols || out->k < rows) return NVFP4_EINVAL;
   } else {
     return NVFP4_EINVAL;
   }
-  if ((rows / 16 + 1) * (cols + 1) > kMaxBlocks || rows * (cols / 16 + 1) > kMaxBlocks) return NVFP4_EUNSUPPORTED;
+  if ((rows / 16 + 1) * (cols + 1) > kMaxBlocks || rows * (cols / 16 + 1) > kMaxBlocks ||
+      (out->k / 16 + 1) * (out->rows + 1) > kMaxBlocks)
+    return NVFP4_EUNSUPPORTED;
   return NVFP4_OK;
 }
 
@@ -116,7 +118,7 @@ int nvfp4_encode(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
   if (axis == 1)
     return from_hip(nvfp4::launch_encode_rows(x, dtype, rows, cols, ld, rows_per_domain, amax, 1, qout(out),
                                               false, 0, s));
-  return from_hip(nvfp4::launch_encode_cols(x, dtype, rows, cols, ld, amax, 1, qout(out), false, 0, s));
+  return from_hip(nvfp4::launch_encode_cols(x, dtype, rows, cols, ld, amax, 1, qout(out), false, 0, s, out->k));
 }
 
 static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int axis,
@@ -142,7 +144,7 @@ static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, i
   }
   if (e != hipSuccess) return NVFP4_EHIP;
   if (axis == 1) e = nvfp4::launch_encode_rows(x, dtype, rows, cols, ld, 0, parts, np, qout(out), rht, mask, s);
-  else e = nvfp4::launch_encode_cols(x, dtype, rows, cols, ld, parts, np, qout(out), rht, mask, s);
+  else e = nvfp4::launch_encode_cols(x, dtype, rows, cols, ld, parts, np, qout(out), rht, mask, s, out->k);
   return from_hip(e);
 }
 

@@ -205,12 +205,16 @@ __device__ __forceinline__ float chunk_elem(const ColChunk<DT>& c, int j) {
   }
 }
 
+//
+// The output rows may be longer than `rows` (out_k >= rows, a multiple of
+// 16): the blocks past `rows` get zero codes and zero scales, which decode to
+// 0 and add nothing to a GEMM over the padded reduction dimension.
 template <int DT, bool RHT, bool AMAX_ONLY>
 __global__ __launch_bounds__(kThreads) void cols_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     const float* __restrict__ parts_in, int nparts_in, float* __restrict__ parts_out,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ tscale,
-    uint32_t mask) {
+    uint32_t mask, int64_t out_k) {
   // Output staging, row-block major with one column of padding so that both
   // the per-thread writes and the per-column reads spread over the banks.
   __shared__ u32x2_t ocodes[AMAX_ONLY ? 1 : kColRB][kColTC + 1];
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(
     S = reduce_parts(parts_in, nparts_in) / kGlobalMax;
     if (blockIdx.x == 0 && threadIdx.x == 0) tscale[0] = S;
   }
-  const int64_t nbc = rows / kBlock;               // blocks per column = per output row
+  const int64_t nbc = out_k / kBlock;              // blocks per output row (>= rows / 16)
   const uint32_t ntr = cdiv(rows, kColTR), ntc = cdiv(cols, kColTC);
   const uint32_t ntiles = ntr * ntc;
   const int t = threadIdx.x, q = t % kColCH, rb = t / kColCH;
@@ -299,6 +303,15 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(
   if constexpr (AMAX_ONLY) {
     m = workgroup_max(m);
     if (threadIdx.x == 0) parts_out[blockIdx.x] = m;
+  } else {
+    // Zero blocks of the padded reduction dimension.
+    const int64_t nb_in = rows / kBlock, npad = nbc - nb_in;
+    const int64_t total = npad * cols;
+    for (int64_t p = (int64_t)blockIdx.x * kThreads + t; p < total; p += (int64_t)gridDim.x * kThreads) {
+      const int64_t orow = p / npad, ob = orow * nbc + nb_in + (p - orow * npad);
+      reinterpret_cast<u32x2_t*>(codes)[ob] = u32x2_t{0u, 0u};
+      scales[ob] = 0;
+    }
   }
 }
 
@@ -411,7 +424,7 @@ hipError_t launch_amax_parts_cols(const void* x, int dt, int64_t rows, int64_t c
                                   float* parts, uint32_t nparts, bool rht, uint32_t mask, hipStream_t s) {
 #define NVFP4_CAMAX(D, R)                                                                        \
   cols_kernel<D, R, true><<<nparts, kThreads, 0, s>>>(x, rows, cols, ld, nullptr, 0, parts, \
-                                                            nullptr, nullptr, nullptr, mask)
+                                                            nullptr, nullptr, nullptr, mask, rows)
   if (dt == 0) { if (rht) NVFP4_CAMAX(0, true); else NVFP4_CAMAX(0, false); }
   else { if (rht) NVFP4_CAMAX(1, true); else NVFP4_CAMAX(1, false); }
 #undef NVFP4_CAMAX
@@ -441,7 +454,8 @@ hipError_t launch_encode_rows(const void* x, int dt, int64_t rows, int64_t cols,
 
 hipError_t launch_encode_cols(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
                               const float* parts, uint32_t nparts, QOut out, bool rht, uint32_t mask,
-                              hipStream_t s) {
+                              hipStream_t s, int64_t out_k) {
+  if (out_k < rows) out_k = rows;
   // Same grid as the amax pass: at most kMaxParts workgroups, so that a
   // tensor of many tiles gives every workgroup the same number of them.
   const int64_t tiles = (int64_t)cdiv(rows, kColTR) * cdiv(cols, kColTC);
@@ -449,7 +463,7 @@ hipError_t launch_encode_cols(const void* x, int dt, int64_t rows, int64_t cols,
 #define NVFP4_ENC_COLS(D, R)                                                                     \
   cols_kernel<D, R, false><<<grid, kThreads, 0, s>>>(x, rows, cols, ld, parts, (int)nparts, \
                                                           nullptr, out.codes, out.scales,        \
-                                                          out.tscale, mask)
+                                                          out.tscale, mask, out_k)
   if (dt == 0) { if (rht) NVFP4_ENC_COLS(0, true); else NVFP4_ENC_COLS(0, false); }
   else { if (rht) NVFP4_ENC_COLS(1, true); else NVFP4_ENC_COLS(1, false); }
 #undef NVFP4_ENC_COLS

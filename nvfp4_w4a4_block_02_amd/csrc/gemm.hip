@@ -24,7 +24,7 @@
 // k = {8s..8s+7} and {64+8s..64+8s+7}.  The MFMA reduction runs over any k as
 // long as A and B use the same assignment, which they do.
 //
-// Main kernel (K a multiple of 128): a 3-stage LDS ring fed by direct
+// Main kernel (K >= 128, K % 64 == 0): a 3-stage LDS ring fed by direct
 // global->LDS loads (global_load_lds_dwordx4 / _dword).  Every K-tile is read
 // from memory once per workgroup; its LDS image is laid out in the order the
 // consuming lanes read it (fragment, 16-byte half, lane), so the ds_reads are
@@ -198,8 +198,46 @@ __device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int band, int&
   tn = n0 + (loc - tm * w);
 }
 
+// Fragments of one K-tile straight from global memory, bounds-checked along
+// K.  This lane owns k in [kt + 64 hh, kt + 64 hh + 64) of its rows: code
+// dword s covers k0 = kt + 64 hh + 8 s (valid iff k0 < K, since K % 16 == 0)
+// and scale byte q covers k0 = kt + 64 hh + 16 q; past K both read as 0, and
+// a zero code decodes to 0.
+template <int FA, int FB>
+__device__ __forceinline__ void load_frags_checked(Frags<FA, FB>& fr, const uint8_t* const (&pa)[FA],
+                                                   const uint8_t* const (&psa)[FA], const uint8_t* const (&pb)[FB],
+                                                   const uint8_t* const (&psb)[FB], int kt, int hh, int K) {
+  const int kl = kt + 64 * hh;
+  auto ld_codes = [&](const uint8_t* row, u32x4_t (&dst)[2]) {
+    uint32_t w[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) w[s] = (kl + 8 * s < K) ? *reinterpret_cast<const uint32_t*>(row + 4 * s) : 0u;
+    dst[0] = u32x4_t{w[0], w[1], w[2], w[3]};
+    dst[1] = u32x4_t{w[4], w[5], w[6], w[7]};
+  };
+  auto ld_scales = [&](const uint8_t* row) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (kl + 16 * q < K) v |= (uint32_t)row[q] << (8 * q);
+    return v;
+  };
+#pragma unroll
+  for (int f = 0; f < FA; ++f) {
+    ld_codes(pa[f] + kt / 2, fr.a[f]);
+    fr.sa[f] = ld_scales(psa[f] + kt / 16);
+  }
+#pragma unroll
+  for (int f = 0; f < FB; ++f) {
+    ld_codes(pb[f] + kt / 2, fr.b[f]);
+    fr.sb[f] = ld_scales(psb[f] + kt / 16);
+  }
+}
+
 // ---------------------------------------------------------------------------
-// Main kernel: K % 128 == 0.
+// Main kernel: K >= 128, K % 64 == 0.  The K / 128 full tiles go through the
+// LDS pipeline; a remainder of 64 is one bounds-checked tile loaded straight
+// into registers at the end.
 //
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
 // lgkmcnt[11:8] | vmcnt[5:4] << 14): wait until at most N vector-memory
@@ -370,13 +408,35 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
   if (t < nt) body(t, F0, F1);
   wait_vmcnt<0>();  // no load into LDS may be in flight when the workgroup ends
 
+  if (K % kKT != 0) {
+    const uint8_t* pa[FA];
+    const uint8_t* psa[FA];
+    const uint8_t* pb[FB];
+    const uint8_t* psb[FB];
+#pragma unroll
+    for (int f = 0; f < FA; ++f) {
+      const int row = min(mwg + wy * 32 * FA + 32 * f + li, M - 1);
+      pa[f] = ac + (int64_t)row * cpitch + 32 * hh;
+      psa[f] = as + (int64_t)row * spitch + 4 * hh;
+    }
+#pragma unroll
+    for (int f = 0; f < FB; ++f) {
+      const int col = min(nwg + wx * 32 * FB + 32 * f + li, N - 1);
+      pb[f] = bc + (int64_t)col * cpitch + 32 * hh;
+      psb[f] = bs + (int64_t)col * spitch + 4 * hh;
+    }
+    Frags<FA, FB> fr;
+    load_frags_checked(fr, pa, psa, pb, psb, nt * kKT, hh, K);
+    compute_tile(fr, acc);
+  }
+
   store_tile<FA, FB, OUT, EPI>(acc, ats[0] * bts[0], mwg + wy * 32 * FA, nwg + wx * 32 * FB, li, hh, M, N, c, ldc,
                                amax_out);
 }
 
 // ---------------------------------------------------------------------------
-// Fallback kernel: any K % 16 == 0 (fragments straight from global memory,
-// bounds-checked along K).
+// Fallback kernel: K < 128, K % 64 != 0 or misaligned operands (fragments
+// straight from global memory, bounds-checked along K).
 template <int FA, int FB, int OUT, int EPI>
 __global__ __launch_bounds__(256) void gemm_checked_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
@@ -411,35 +471,8 @@ __global__ __launch_bounds__(256) void gemm_checked_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   for (int kt = 0; kt < K; kt += kKT) {
-    // This lane owns k in [kt + 64 hh, kt + 64 hh + 64); code dword s covers
-    // k0 = kt + 64 hh + 8 s (valid iff k0 < K, since K % 16 == 0) and scale
-    // byte q covers k0 = kt + 64 hh + 16 q.
-    const int kl = kt + 64 * hh;
     Frags<FA, FB> fr;
-    auto ld_codes = [&](const uint8_t* row, u32x4_t (&dst)[2]) {
-      uint32_t w[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) w[s] = (kl + 8 * s < K) ? *reinterpret_cast<const uint32_t*>(row + 4 * s) : 0u;
-      dst[0] = u32x4_t{w[0], w[1], w[2], w[3]};
-      dst[1] = u32x4_t{w[4], w[5], w[6], w[7]};
-    };
-    auto ld_scales = [&](const uint8_t* row) {
-      uint32_t v = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (kl + 16 * q < K) v |= (uint32_t)row[q] << (8 * q);
-      return v;
-    };
-#pragma unroll
-    for (int f = 0; f < FA; ++f) {
-      ld_codes(pa[f] + kt / 2, fr.a[f]);
-      fr.sa[f] = ld_scales(psa[f] + kt / 16);
-    }
-#pragma unroll
-    for (int f = 0; f < FB; ++f) {
-      ld_codes(pb[f] + kt / 2, fr.b[f]);
-      fr.sb[f] = ld_scales(psb[f] + kt / 16);
-    }
+    load_frags_checked(fr, pa, psa, pb, psb, kt, hh, K);
     compute_tile(fr, acc);
   }
   store_tile<FA, FB, OUT, EPI>(acc, ats[0] * bts[0], m0, n0, li, hh, M, N, c, ldc, amax_out);
@@ -517,7 +550,10 @@ hipError_t launch_gemm(QOut a, QOut b, int64_t m, int64_t n, int64_t k, void* c,
     if (e != hipSuccess) return e;
   }
   const Args g{a, b, (int)m, (int)n, (int)k, c, ldc, amax_out};
-  const bool lds_path = (k % kKT == 0) && ((uintptr_t)a.codes % 16 == 0) && ((uintptr_t)b.codes % 16 == 0) &&
+  // LDS path: K >= 128 and K % 64 == 0, so every code row starts 16-byte
+  // aligned and every scale row 4-byte aligned (the direct-to-LDS loads need
+  // both); a remainder of 64 goes through the checked tail tile.
+  const bool lds_path = (k >= kKT) && (k % 64 == 0) && ((uintptr_t)a.codes % 16 == 0) && ((uintptr_t)b.codes % 16 == 0) &&
                         ((uintptr_t)a.scales % 4 == 0) && ((uintptr_t)b.scales % 4 == 0);
   if (lds_path) {
     int fa = tile_fa, fb = tile_fb;

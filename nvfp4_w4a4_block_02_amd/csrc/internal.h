@@ -42,9 +42,10 @@ hipError_t launch_reduce_parts(const float* parts, uint32_t nparts, int64_t ndom
 hipError_t launch_encode_rows(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
                               int64_t rows_per_domain, const float* parts, uint32_t nparts, QOut out,
                               bool rht, uint32_t mask, hipStream_t s, bool four_over_six = false);
+// out_k: length of the output rows (>= rows; blocks past rows are zeroed).
 hipError_t launch_encode_cols(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
                               const float* parts, uint32_t nparts, QOut out, bool rht, uint32_t mask,
-                              hipStream_t s);
+                              hipStream_t s, int64_t out_k = 0);
 
 // Step 7.
 hipError_t launch_dequant(QOut in, int64_t rows, int64_t k, int64_t rows_per_domain, void* out,

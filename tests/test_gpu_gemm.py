@@ -52,7 +52,8 @@ def test_gemm_matches_oracle(nv, m, n, k, out):
 
 
 @pytest.mark.parametrize("tiles", [(2, 4), (4, 2), (3, 3), (4, 4)])
-@pytest.mark.parametrize("m,n,k", [(300, 520, 384), (97, 1100, 1280), (1030, 70, 256)])
+@pytest.mark.parametrize("m,n,k", [(300, 520, 384), (97, 1100, 1280), (1030, 70, 256), (200, 330, 192),
+                                   (65, 300, 1344)])
 def test_gemm_every_tile_shape(nv, tiles, m, n, k):
     log(f"gemm tiles {tiles} {m}x{n}x{k}")
     rng = np.random.default_rng(m + n + k + 10 * tiles[0])
@@ -197,3 +198,37 @@ def test_wgrad_after_rht_full(nv):
     rows = np.unique(np.concatenate([[0, 3071], np.random.default_rng(5).integers(0, 3072, 64)]))
     cref, bound = oracle.gemm_ref(og, ox, rows=rows)
     assert_gemm_close(c[rows], cref, bound, False, "workload 5")
+
+
+@pytest.mark.timeout(600)
+def test_train_linear_triple_full(nv):
+    """Workload 6 (the training slice of the attention projection): forward,
+    input gradient and weight gradient, every operand bit-exact against the
+    oracle's quantizers and every GEMM within the parity bound on sampled rows."""
+    d = workloads.train_linear()
+    log("workload 6: training triple of a 2640x3072x3072 linear layer")
+    x, w, dy = dev_bf16(d["x"]), dev_f32(d["w"]), dev_bf16(d["dy"])
+    y, dx, dw = nv.linear_train(x, w, dy, d["mask"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    rows = {"m": np.unique(np.concatenate([[0, 2639], rng.integers(0, 2640, 40)])),
+            "n": np.unique(np.concatenate([[0, 3071], rng.integers(0, 3072, 40)]))}
+    r = oracle.linear_train_ref(widen(d["x"]), d["w"], widen(d["dy"]), d["mask"], rows=rows)
+    # the quantized operands, recomputed through the same entry points
+    assert_q_exact(nv.quantize(x), r["xq"], "X")
+    assert_q_exact(nv.quantize(w), r["wq"], "W")
+    assert_q_exact(nv.quantize(dy), r["dyq"], "dY")
+    assert_q_exact(nv.quantize(w, axis=0), r["wtq"], "W along dim 0")
+    assert_q_exact(nv.rht16_quantize(dy, d["mask"], axis=0), r["dyt"], "RHT dY along dim 0")
+    assert_q_exact(nv.rht16_quantize(x, d["mask"], axis=0), r["xt"], "RHT X along dim 0")
+    # the padded operands linear_train feeds the weight-gradient GEMM (M = 2640
+    # padded to 2688): the oracle's bytes, then zero codes and zero scales
+    for src, want, tag in ((dy, r["dyt"], "dY"), (x, r["xt"], "X")):
+        gp = nv.rht16_quantize(src, d["mask"], axis=0, k_pad=2688)
+        codes, scales = gp.codes.cpu().numpy(), gp.scales.cpu().numpy()
+        assert np.array_equal(codes[:, :1320], want.codes) and not codes[:, 1320:].any(), tag
+        assert np.array_equal(scales[:, :165], want.scales) and not scales[:, 165:].any(), tag
+        assert gp.tscale.cpu().numpy()[0] == want.tscale[0], tag
+    assert_gemm_close(y.float().cpu().numpy()[rows["m"]], r["y"], r["by"], True, "forward")
+    assert_gemm_close(dx.float().cpu().numpy()[rows["m"]], r["dx"], r["bdx"], True, "input gradient")
+    assert_gemm_close(dw.cpu().numpy()[rows["n"]], r["dw"], r["bdw"], False, "weight gradient")
