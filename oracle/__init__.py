@@ -30,6 +30,9 @@ Sources.  The format is defined by the LongLive-2.0 pages:
   reading).
 * hyper.ai summary of the LongLive-2.0 paper, section "方法": the KV cache is
   quantized per block of eight frames and rebuilt by a parallel dequant kernel.
+* 171host.com, "LongLive 2.0 技术拆解", section 2.2: attention runs over 9
+  local latent frames plus 3 sink frames kept in the cache, frame-causally
+  (``attention.py`` states the reading).
 
 Everything finer (E4M3 as the FP8 flavour, the scale recipe, rounding, nibble
 order, layouts, the RHT normalisation) is a reading where the pages are silent;
@@ -68,6 +71,7 @@ from .codec import (  # noqa: F401
 from .rht import hadamard16, sign_vector, rht16_rows, rht16_quantize  # noqa: F401
 from .gemm import gemm_ref, gelu_tanh, ffn_chain  # noqa: F401
 from .train import linear_train_ref  # noqa: F401
+from .attention import decode_kv, key_visibility, window_attention_ref  # noqa: F401
 from .four_over_six import (  # noqa: F401
     block_scales_to,
     block_sq_error,

@@ -35,6 +35,7 @@ WORKLOADS = {
     4: "kv_codec_12x880x24x128",
     5: "rht_wgrad_16384x3072",
     6: "train_linear_2640x3072x3072",
+    7: "kv_window_attention_2640q_12x880x24x128",
 }
 
 
@@ -118,3 +119,16 @@ def train_linear(m=2640, n=3072, k=3072, seed=1006, mask_seed=2006):
     dy = _outliers(rng, rng.laplace(0.0, 1e-3, size=(m, n)).astype(np.float32), 0.001, 100.0)
     mask = int(np.random.default_rng(mask_seed).integers(0, 2 ** 16))
     return {"x": to_bf16_bits(x), "w": w, "dy": to_bf16_bits(dy), "mask": mask}
+
+
+def window_attention(frames=12, tokens=880, heads=24, head_dim=128, q_frames=3, seed=1007):
+    """Workload 7: the K/V cache of workload 4 (3 sink + 9 window frames)
+    plus the queries of the chunk being denoised: bf16 [q_frames * tokens,
+    heads, head_dim] ~N(0,1) with a per-head std log-uniform in [0.5, 2]."""
+    out = kv_cache(frames, tokens, heads, head_dim, seed=seed + 1)
+    rng = np.random.default_rng(seed)
+    std = np.exp(rng.uniform(np.log(0.5), np.log(2.0), size=heads)).astype(np.float32)
+    q = rng.standard_normal((q_frames * tokens, heads, head_dim), dtype=np.float32)
+    q *= std[None, :, None]
+    out["q"] = to_bf16_bits(q)
+    return out
