@@ -233,6 +233,42 @@ int nvfp4_kv_dequant(const nvfp4_tensor *in, int64_t frames, int64_t tokens, int
                      int64_t head_dim, int64_t frame_block, void *out, void *stream);
 
 /*
+ * Frame-causal window attention that reads the NVFP4 KV cache directly (the
+ * consumer of the cache: 9 local latent frames plus 3 sink frames kept in the
+ * cache, 171host.com "LongLive 2.0 技术拆解", section 2.2; NVFP4 cache in
+ * 8-frame blocks, hyper.ai LongLive-2.0 summary, "方法").  K and V tiles are
+ * decoded in on-chip memory inside the attention loop; no bf16 copy of the
+ * window is written.
+ *
+ *   q    device bf16 [q_frames * tokens][heads][head_dim], contiguous: the
+ *        queries of the last q_frames frames of the window (the chunk being
+ *        generated);
+ *   k, v NVFP4 caches as written by nvfp4_kv_quant / nvfp4_kv_quant_4over6
+ *        (rows = frames * tokens * heads, k = head_dim, one tensor scale per
+ *        frame block);
+ *   out  device [q_frames * tokens][heads][head_dim], out_dtype NVFP4_F32 or
+ *        NVFP4_BF16 (round-to-nearest-even), contiguous.
+ *
+ * Query i sits in window frame f = frames - q_frames + i / tokens and attends
+ * to every key of frames 0..f (its own frame included, no later frame):
+ *   out[i][h] = sum_j softmax_j(q[i][h] . K[j][h] / sqrt(head_dim)) V[j][h],
+ * K, V = e2m1 * s_b * S exactly.  Products run on fp16 MFMA with float32
+ * accumulation (decoded elements are exact in fp16; q enters with a per-row
+ * power-of-two scale); probabilities are rounded to fp16.  Results agree with
+ * an exact computation to about 2^-10 of sum_j p_j |V_j| / sum_j p_j per
+ * element (plus the bf16 rounding of the output).
+ *
+ * Limits: head_dim must be 128 (else NVFP4_EUNSUPPORTED); 1 <= q_frames <=
+ * frames; with more than one frame block, frame_block * tokens must be a
+ * multiple of 32 (each 32-key block lies in one frame block; else
+ * NVFP4_EUNSUPPORTED).  A non-finite value anywhere in the keys a workgroup
+ * of 128 queries scans can propagate to its outputs.  No workspace.
+ */
+int nvfp4_kv_attention(const void *q, int64_t q_frames, const nvfp4_tensor *k, const nvfp4_tensor *v,
+                       int64_t frames, int64_t tokens, int64_t heads, int64_t head_dim,
+                       int64_t frame_block, void *out, int out_dtype, void *stream);
+
+/*
  * Plain dequantization (decode step), float32 or bf16 output [rows][k],
  * contiguous; rows_per_domain as in nvfp4_amax (0 = one domain).
  */

@@ -63,6 +63,7 @@ def _load():
         "nvfp4_kv_quant_4over6": (I, [P, I64, I64, I64, I64, I64, TP, P, SZ, P]),
         "nvfp4_kv_dequant": (I, [TP, I64, I64, I64, I64, I64, P, P]),
         "nvfp4_dequantize": (I, [TP, I64, P, I, P]),
+        "nvfp4_kv_attention": (I, [P, I64, TP, TP, I64, I64, I64, I64, I64, P, I, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -89,7 +90,7 @@ def __getattr__(name):  # module attribute `lib` loads the library on first acce
 
 EXPORTED = ("nvfp4_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_amax",
             "nvfp4_encode", "nvfp4_quantize", "rht16_quantize", "nvfp4_gemm", "nvfp4_gemm_tiled", "nvfp4_kv_quant",
-            "nvfp4_kv_quant_4over6", "nvfp4_kv_dequant", "nvfp4_dequantize")
+            "nvfp4_kv_quant_4over6", "nvfp4_kv_dequant", "nvfp4_dequantize", "nvfp4_kv_attention")
 
 
 def _check(status: int, what: str):
@@ -268,6 +269,24 @@ def kv_dequant(q: NVFP4Tensor, shape, frame_block: int = 8, out: torch.Tensor | 
     ct = q.c()
     _check(_lib().nvfp4_kv_dequant(ctypes.byref(ct), f, t, h, d, frame_block, _ptr(out), _stream(stream)),
            "nvfp4_kv_dequant")
+    return out
+
+
+def kv_attention(q: torch.Tensor, k: NVFP4Tensor, v: NVFP4Tensor, shape, frame_block: int = 8,
+                 out_dtype=torch.bfloat16, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Frame-causal window attention of ``q`` (bf16 [q_frames * tokens, heads,
+    head_dim]) over the NVFP4 caches ``k``/``v`` of ``shape`` = (frames, tokens,
+    heads, head_dim) (nvfp4_kv_attention)."""
+    f, t, h, d = shape
+    if q.dtype != torch.bfloat16 or not q.is_contiguous() or q.dim() != 3 or q.shape[1:] != (h, d) \
+            or t == 0 or q.shape[0] % t:
+        raise TypeError("q must be a contiguous bfloat16 tensor [q_frames * tokens, heads, head_dim]")
+    qf = q.shape[0] // t
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    ck, cv = k.c(), v.c()
+    _check(_lib().nvfp4_kv_attention(_ptr(q), qf, ctypes.byref(ck), ctypes.byref(cv), f, t, h, d, frame_block,
+                                     _ptr(out), _dtype_code(out), _stream(stream)), "nvfp4_kv_attention")
     return out
 
 

@@ -232,6 +232,29 @@ int nvfp4_kv_dequant(const nvfp4_tensor* in, int64_t frames, int64_t tokens, int
                                         (hipStream_t)stream));
 }
 
+int nvfp4_kv_attention(const void* q, int64_t q_frames, const nvfp4_tensor* k, const nvfp4_tensor* v,
+                       int64_t frames, int64_t tokens, int64_t heads, int64_t head_dim, int64_t frame_block,
+                       void* out, int out_dtype, void* stream) {
+  if (!q || !out || !aligned16(q) || !aligned16(out) || !valid_dtype(out_dtype) || frames < 0 || tokens < 0 ||
+      heads < 0 || head_dim < 0 || head_dim % 16 != 0 || frame_block <= 0 || q_frames < 0 || q_frames > frames)
+    return NVFP4_EINVAL;
+  const int64_t rows = frames * tokens * heads;
+  if (!tensor_ok(k) || !tensor_ok(v) || k->rows != rows || v->rows != rows || k->k != head_dim ||
+      v->k != head_dim)
+    return NVFP4_EINVAL;
+  const int64_t nq = q_frames * tokens;
+  if (nq == 0 || heads == 0) return NVFP4_OK;
+  if (head_dim != 128) return NVFP4_EUNSUPPORTED;
+  const int64_t nfb = (frames + frame_block - 1) / frame_block;
+  if (nfb > 1 && (frame_block * tokens) % 32 != 0) return NVFP4_EUNSUPPORTED;
+  // 32-bit offsets: code bytes of the cache and the workgroup count
+  if (rows * 64 >= ((int64_t)1 << 31) || ((nq + 127) / 128) * heads >= ((int64_t)1 << 31))
+    return NVFP4_EUNSUPPORTED;
+  return from_hip(nvfp4::launch_kv_attention(static_cast<const uint16_t*>(q), qout(k), qout(v), out,
+                                             out_dtype == NVFP4_F32, nq, tokens, heads, frames, q_frames,
+                                             frame_block, (hipStream_t)stream));
+}
+
 int nvfp4_dequantize(const nvfp4_tensor* in, int64_t rows_per_domain, void* out, int dtype, void* stream) {
   if (!tensor_ok(in) || !out || !aligned16(out) || !valid_dtype(dtype) || rows_per_domain < 0)
     return NVFP4_EINVAL;

@@ -56,4 +56,9 @@ hipError_t launch_gemm(QOut a, QOut b, int64_t m, int64_t n, int64_t k, void* c,
                        int64_t ldc, int epilogue, float* amax_out, int tile_fa, int tile_fb, hipStream_t s);
 bool gemm_tiles_supported(int tile_fa, int tile_fb);
 
+// Frame-causal window attention over an NVFP4 KV cache (head_dim 128).
+hipError_t launch_kv_attention(const uint16_t* q, QOut k, QOut v, void* out, int out_f32, int64_t nq,
+                               int64_t tokens, int64_t heads, int64_t frames, int64_t q_frames,
+                               int64_t frame_block, hipStream_t s);
+
 }  // namespace nvfp4

@@ -161,3 +161,33 @@ def test_amax_encode_dequant_reject_bad_arguments(nv):
     assert dq(ctypes.byref(good), 0, None, 0, _stream()) == -1
     assert dq(ctypes.byref(good), 0, ctypes.c_void_p(FAKE), 3, _stream()) == -1
     assert dq(ctypes.byref(_t(nv, 0, 32)), 0, ctypes.c_void_p(FAKE), 0, _stream()) == 0
+
+
+def test_kv_attention_rejects_bad_arguments(nv):
+    at = nv.lib.nvfp4_kv_attention
+    F, W = FAKE, ctypes.c_void_p(FAKE)
+    k = _t(nv, 12 * 40 * 2, 128)
+    ok = dict(q=W, qf=3, k=k, v=k, frames=12, tokens=40, heads=2, d=128, fb=8, out=W, dt=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return at(a["q"], a["qf"], ctypes.byref(a["k"]), ctypes.byref(a["v"]), a["frames"], a["tokens"],
+                  a["heads"], a["d"], a["fb"], a["out"], a["dt"], _stream())
+
+    EINVAL, EUNS = -1, -2
+    assert call(q=None) == EINVAL
+    assert call(q=ctypes.c_void_p(F + 2)) == EINVAL
+    assert call(out=None) == EINVAL
+    assert call(dt=4) == EINVAL
+    assert call(qf=13) == EINVAL                              # more query frames than the window
+    assert call(fb=0) == EINVAL
+    assert call(k=_t(nv, 12 * 40 * 2 - 1, 128)) == EINVAL     # cache rows
+    assert call(v=_t(nv, 12 * 40 * 2, 64)) == EINVAL          # head_dim mismatch
+    assert call(k=_t(nv, 12 * 40 * 2, 64), v=_t(nv, 12 * 40 * 2, 64), d=64) == EUNS
+    # 8-frame blocks of 13 tokens = 104 keys: not 32-key aligned, two blocks
+    k13 = _t(nv, 12 * 13 * 2, 128)
+    assert call(k=k13, v=k13, tokens=13) == EUNS
+    # a single frame block needs no alignment; zero queries is a no-op
+    k13b = _t(nv, 5 * 13 * 2, 128)
+    assert call(k=k13b, v=k13b, frames=5, tokens=13, qf=0) == 0
+    assert call(qf=0) == 0
