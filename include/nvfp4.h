@@ -260,7 +260,7 @@ int nvfp4_kv_dequant(const nvfp4_tensor *in, int64_t frames, int64_t tokens, int
  *
  * Limits: head_dim must be 128 (else NVFP4_EUNSUPPORTED); 1 <= q_frames <=
  * frames; with more than one frame block, frame_block * tokens must be a
- * multiple of 32 (each 32-key block lies in one frame block; else
+ * multiple of 64 (each 64-key tile lies in one frame block; else
  * NVFP4_EUNSUPPORTED).  A non-finite value anywhere in the keys a workgroup
  * of 128 queries scans can propagate to its outputs.  No workspace.
  */

@@ -246,7 +246,7 @@ int nvfp4_kv_attention(const void* q, int64_t q_frames, const nvfp4_tensor* k, c
   if (nq == 0 || heads == 0) return NVFP4_OK;
   if (head_dim != 128) return NVFP4_EUNSUPPORTED;
   const int64_t nfb = (frames + frame_block - 1) / frame_block;
-  if (nfb > 1 && (frame_block * tokens) % 32 != 0) return NVFP4_EUNSUPPORTED;
+  if (nfb > 1 && (frame_block * tokens) % 64 != 0) return NVFP4_EUNSUPPORTED;
   // 32-bit offsets: code bytes of the cache and the workgroup count
   if (rows * 64 >= ((int64_t)1 << 31) || ((nq + 127) / 128) * heads >= ((int64_t)1 << 31))
     return NVFP4_EUNSUPPORTED;

@@ -77,7 +77,56 @@ struct Geo {
   const uint8_t* vc;
   const uint8_t* vs;
   int heads, h, nkeys;
+  // byte offsets of this lane's code loads from the first code row of a tile
+  // (scale offsets are these >> 3: 64 code bytes and 8 scale bytes per row)
+  uint32_t okc, ovc[4];
 };
+
+__device__ __forceinline__ void init_geo(Geo& g, int tid) {
+  const uint32_t rb = (uint32_t)g.heads * 64u;       // code bytes between consecutive keys
+  g.okc = (uint32_t)(tid & 63) * rb + 16u * (uint32_t)(tid >> 6);
+  const int kg = tid & 15, dc = tid >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) g.ovc[i] = (uint32_t)(4 * kg + i) * rb + 4u * (uint32_t)dc;
+}
+
+// Raw codes of K tile key0 (32 code bytes + 2 scale bytes per lane).
+__device__ __forceinline__ void load_raw_k(const Geo& g, int key0, int tid, Raw& r) {
+  if (key0 + kKT <= g.nkeys) {
+    const uint32_t row0 = (uint32_t)key0 * (uint32_t)g.heads + (uint32_t)g.h;
+    r.kc = *reinterpret_cast<const u32x4_t*>(g.kc + (size_t)row0 * 64u + g.okc);
+    r.ks = *reinterpret_cast<const uint16_t*>(g.ks + (size_t)row0 * 8u + (g.okc >> 3));
+    return;
+  }
+  // last, partial tile: rows past the end re-read the last key (masked)
+  const int key = min(key0 + (tid & 63), g.nkeys - 1);
+  const uint32_t row = (uint32_t)key * (uint32_t)g.heads + (uint32_t)g.h;
+  r.kc = *reinterpret_cast<const u32x4_t*>(g.kc + row * 64u + 16u * (uint32_t)(tid >> 6));
+  r.ks = *reinterpret_cast<const uint16_t*>(g.ks + row * 8u + 2u * (uint32_t)(tid >> 6));
+}
+
+// Raw codes of V tile key0 (4 keys x 8 elements per lane).
+__device__ __forceinline__ void load_raw_v(const Geo& g, int key0, int tid, Raw& r) {
+  if (key0 + kKT <= g.nkeys) {
+    const uint32_t row0 = (uint32_t)key0 * (uint32_t)g.heads + (uint32_t)g.h;
+    const uint8_t* vcb = g.vc + (size_t)row0 * 64u;
+    const uint8_t* vsb = g.vs + (size_t)row0 * 8u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r.vc[i] = *reinterpret_cast<const uint32_t*>(vcb + g.ovc[i]);
+      r.vs[i] = vsb[g.ovc[i] >> 3];
+    }
+    return;
+  }
+  const int kg = tid & 15, dc = tid >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = min(key0 + 4 * kg + i, g.nkeys - 1);
+    const uint32_t row = (uint32_t)key * (uint32_t)g.heads + (uint32_t)g.h;
+    r.vc[i] = *reinterpret_cast<const uint32_t*>(g.vc + row * 64u + 4u * dc);
+    r.vs[i] = g.vs[row * 8u + (dc >> 1)];
+  }
+}
 
 __device__ __forceinline__ half8_t decode8(uint32_t codes, half2_t sig2) {
   const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * sig2;
@@ -88,24 +137,6 @@ __device__ __forceinline__ half8_t decode8(uint32_t codes, half2_t sig2) {
   r[0] = p0.x; r[1] = p0.y; r[2] = p1.x; r[3] = p1.y;
   r[4] = p2.x; r[5] = p2.y; r[6] = p3.x; r[7] = p3.y;
   return r;
-}
-
-__device__ __forceinline__ void load_raw(const Geo& g, int key0, int tid, Raw& r) {
-  const int wave = tid >> 6;
-  {
-    const int key = min(key0 + (tid & 63), g.nkeys - 1);
-    const uint32_t row = (uint32_t)key * (uint32_t)g.heads + (uint32_t)g.h;
-    r.kc = *reinterpret_cast<const u32x4_t*>(g.kc + row * 64u + 16u * wave);
-    r.ks = *reinterpret_cast<const uint16_t*>(g.ks + row * 8u + 2u * wave);
-  }
-  const int kg = tid & 15, dc = tid >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = min(key0 + 4 * kg + i, g.nkeys - 1);
-    const uint32_t row = (uint32_t)key * (uint32_t)g.heads + (uint32_t)g.h;
-    r.vc[i] = *reinterpret_cast<const uint32_t*>(g.vc + row * 64u + 4u * dc);
-    r.vs[i] = g.vs[row * 8u + (dc >> 1)];
-  }
 }
 
 // K tile, row-major: K_lds[key][d], fp16, row pitch kKRow.
@@ -161,103 +192,174 @@ __device__ __forceinline__ void decode_v(const Raw& r, uint8_t* buf, int tid) {
   v_byte<3>(lo01, hi01, lo23, hi23, s01, s23, dst);
 }
 
-// Per-query-column state of a wavefront (two 32-query columns g = 0, 1).
+// Softmax and output state of one wavefront (32 queries, one per lane column).
 struct State {
-  float16_t acc[2][4];   // O^T: column g, d block db (32 d), in units of svref
-  float m[2];            // running maximum (base 2), equal in lanes c and c + 32
-  float l[2];            // partial row sum over this lane's keys
-  float svref;           // V tensor scale the accumulator is expressed in (0: none yet)
+  float16_t acc[4];   // O^T for d block db (32 d), in units of svref
+  float m;            // running maximum of the scaled scores (base 2), equal in lanes c and c + 32
+  float l;            // partial row sum over this lane's keys
+  float svref;        // V tensor scale the accumulator is expressed in (0: none yet)
 };
 
-template <int G>
-__device__ __forceinline__ void softmax_col(float16_t& s, float c, bool masked, int key_base, int hf, int lim,
-                                            State& st, half8_t& p0, half8_t& p1) {
+// S^T = K Q^T for one 64-key tile (two 32-key blocks) of the wavefront's 32
+// queries; kbuf holds the decoded K tile.
+__device__ __forceinline__ void qk_tile(const uint8_t* kbuf, int c, int hf, const half8_t (&qf)[8],
+                                        float16_t (&sacc)[2]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { sacc[0][i] = 0.0f; sacc[1][i] = 0.0f; }
+  const uint8_t* ka = kbuf + c * kKRow + 16 * hf;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const half8_t a0 = *reinterpret_cast<const half8_t*>(ka + 32 * s);
+    const half8_t a1 = *reinterpret_cast<const half8_t*>(ka + 32 * kKRow + 32 * s);
+    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qf[s], sacc[0], 0, 0, 0);
+    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, qf[s], sacc[1], 0, 0, 0);
+  }
+}
+
+// Online softmax of one tile's scores (the tile lies in one frame block: sk is
+// its K tensor scale).  Produces the fp16 probabilities and returns the factor
+// the accumulator must be multiplied by before they are added (1 unless the
+// running maximum moved).  MASK: apply the per-query key limit.
+template <bool MASK>
+__device__ __forceinline__ float softmax_tile(float16_t (&sacc)[2], int key0, int hf, float cq, int lim, float sk,
+                                              State& st, half8_t (&pb)[2][2]) {
+  // Scaled scores s = raw * cs, rounded to float32 first and the maximum
+  // taken over those same values, so the maximum's exponent is exactly 0 at
+  // any magnitude (an fma against a rounded maximum would leave a residual
+  // of up to half an ulp of it: beyond 2^24 enough to overflow or flush every
+  // probability).  Contraction of s - m into an fma is therefore off here.
+  // Masked keys become -inf.
+#pragma clang fp contract(off)
+  const float cs = cq * sk;
+  const int rel = lim - key0 - 4 * hf;   // key offset limit of this lane's elements
   float mt = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float v = s[i] * c;
-    if (masked) {
-      const int key = key_base + 8 * (i >> 2) + 4 * hf + (i & 3);
-      v = key < lim ? v : -INFINITY;
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float v = sacc[b][i] * cs;
+      if (MASK) v = (32 * b + 8 * (i >> 2) + (i & 3)) < rel ? v : -INFINITY;
+      sacc[b][i] = v;
+      mt = fmaxf(mt, v);
     }
-    s[i] = v;
-    mt = fmaxf(mt, v);
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));   // the pair of lanes holding one query
+  const float mnew = fmaxf(st.m, mt);
+  const bool need = mnew > st.m + kLazy;
+  const float alpha = need ? __builtin_amdgcn_exp2f(st.m - mnew) : 1.0f;
+  st.m = need ? mnew : st.m;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    pb[0][i >> 3][i & 7] = (_Float16)__builtin_amdgcn_exp2f(sacc[0][i] - st.m);
+    pb[1][i >> 3][i & 7] = (_Float16)__builtin_amdgcn_exp2f(sacc[1][i] - st.m);
   }
-  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-  const float mnew = fmaxf(st.m[G], mt);
-  const bool need = mnew > st.m[G] + kLazy;
-  if (__ballot(need)) {
-    const float alpha = need ? __builtin_amdgcn_exp2f(st.m[G] - mnew) : 1.0f;
-    st.m[G] = need ? mnew : st.m[G];
-    st.l[G] *= alpha;
+  // Row sum of the rounded probabilities, the values the numerator uses:
+  // fp16 pairs dotted with (1, 1) into float32 accumulators.
+  const half2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+  float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      sa = __builtin_amdgcn_fdot2(half2_t{pb[0][u][2 * k], pb[0][u][2 * k + 1]}, one2, sa, false);
+      sb = __builtin_amdgcn_fdot2(half2_t{pb[1][u][2 * k], pb[1][u][2 * k + 1]}, one2, sb, false);
+    }
+  st.l = st.l * alpha + (sa + sb);
+  // materialize the probabilities here, ahead of the rescale branch, so they
+  // are computed alongside the next tile's score MFMAs
+  __asm__ volatile("" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]));
+  return alpha;
+}
+
+__device__ __forceinline__ void rescale(State& st, float f) {
+  if (__ballot(f != 1.0f)) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) st.acc[G][db][i] *= alpha;
-  }
-  const float mref = st.m[G];
-  float sum = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float p = __builtin_amdgcn_exp2f(s[i] - mref);
-    sum += p;
-    if (i < 8) p0[i] = (_Float16)p; else p1[i - 8] = (_Float16)p;
-  }
-  st.l[G] += sum;
-}
-
-// Merge the partner wavefront's partial (other key parity) for column G and
-// write the 32 queries x 128 d of that column.
-template <int G, bool F32OUT>
-__device__ __forceinline__ void finish_col(const State& st, const float* part, int lane, int64_t qrow, bool valid,
-                                           void* __restrict__ out) {
-  const int hf = lane >> 5;
-  const float m1 = part[64 * 64 + lane], l1 = part[64 * 64 + 64 + lane], sv1 = part[64 * 64 + 128 + lane];
-  const float l0 = st.l[G] + __shfl_xor(st.l[G], 32, 64);
-  const float m0 = st.m[G];
-  const float M = fmaxf(m0, m1);
-  const float e0 = __builtin_amdgcn_exp2f(m0 - M), e1 = __builtin_amdgcn_exp2f(m1 - M);
-  const float inv = 1.0f / (l0 * e0 + l1 * e1);
-  const float a0 = st.svref * e0 * inv, a1 = sv1 * e1 * inv;
-  if (!valid) return;
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      float v[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 4 * i4 + r;
-        v[r] = st.acc[G][db][i] * a0 + part[(db * 16 + i) * 64 + lane] * a1;
-      }
-      const int d = 32 * db + 8 * i4 + 4 * hf;
-      if constexpr (F32OUT) {
-        float4_t w = {v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<float4_t*>(static_cast<float*>(out) + qrow * kD + d) = w;
-      } else {
-        u32x2_t w;
-        w[0] = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-        w[1] = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-        *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + qrow * kD + d) = w;
-      }
-    }
+      for (int i = 0; i < 16; ++i) st.acc[db][i] *= f;
   }
 }
 
-// Store column G of this wavefront's partial for the partner to merge.
-template <int G>
-__device__ __forceinline__ void stash_col(const State& st, float* part, int lane) {
+// O^T += V^T P^T for one tile; vbuf holds the decoded, transposed V tile.
+__device__ __forceinline__ void pv_tile(const uint8_t* vbuf, int c, int hf, const half8_t (&pb)[2][2], State& st) {
+  const uint8_t* va = vbuf + c * kVRow + 16 * hf;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) part[(db * 16 + i) * 64 + lane] = st.acc[G][db][i];
-  part[64 * 64 + lane] = st.m[G];
-  part[64 * 64 + 64 + lane] = st.l[G] + __shfl_xor(st.l[G], 32, 64);
-  part[64 * 64 + 128 + lane] = st.svref;
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const half8_t a = *reinterpret_cast<const half8_t*>(va + (32 * db) * kVRow + 64 * b + 32 * u);
+        st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[b][u], st.acc[db], 0, 0, 0);
+      }
+}
+
+struct Ctx {
+  uint8_t* smem;
+  int nt, c, hf, tid, lim, fb_keys;
+  float cq;
+  const float* kts;
+  const float* vts;
+};
+
+// Loop iteration t (software-pipelined by one tile on the K side): the scores
+// of tile t+1 are computed while tile t's softmax runs, and tile t's P V
+// product overlaps the decode of K tile t+2 and V tile t+1 (raw codes loaded
+// one iteration earlier), after which K t+3 and V t+2 are loaded.  Buffers:
+// K and V tile u live in buffer u & 1; a tile is decoded one iteration after
+// the buffer's previous tile was last read, with one barrier per iteration.
+template <bool MASK>
+__device__ __forceinline__ void step(const Ctx& x, int t, const half8_t (&qf)[8], const Geo& geo, Raw& raw,
+                                     float16_t (&scur)[2], State& st) {
+  uint8_t* b0 = x.smem + (t & 1) * kBuf;        // K t+2 (write), V t (read)
+  uint8_t* b1 = x.smem + ((t + 1) & 1) * kBuf;  // K t+1 (read), V t+1 (write)
+  const int key0 = t * kKT;
+  const int fb = key0 / x.fb_keys;
+  // A new V tensor scale (once per frame block): re-express the accumulator
+  // in it.  An all-zero V frame block (scale 0) decodes to zeros and keeps
+  // the unit.
+  const float sv = x.vts[fb];
+  if (sv != 0.0f && sv != st.svref) {
+    if (st.svref != 0.0f) rescale(st, st.svref / sv);
+    st.svref = sv;
+  }
+  // Region 1: scores of tile t+1 (MFMA) under the softmax of tile t (VALU).
+  // On the last tile the scores are computed from a stale buffer and unused.
+  float16_t snext[2];
+  qk_tile(b1, x.c, x.hf, qf, snext);
+  half8_t pb[2][2];
+  const float f = softmax_tile<MASK>(scur, key0, x.hf, x.cq, x.lim, x.kts[fb], st, pb);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  rescale(st, f);
+  // Region 2: P V of tile t (MFMA) under the decode of K t+2 and V t+1 (VALU
+  // and LDS writes).  Buffers past the last tile are rewritten harmlessly.
+  pv_tile(b0 + kKBuf, x.c, x.hf, pb, st);
+  decode_k(raw, b0, x.tid);
+  decode_v(raw, b1, x.tid);
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (t + 3 < x.nt) load_raw_k(geo, (t + 3) * kKT, x.tid, raw);
+  if (t + 2 < x.nt) load_raw_v(geo, (t + 2) * kKT, x.tid, raw);
+  __syncthreads();
+  scur[0] = snext[0];
+  scur[1] = snext[1];
 }
 
 template <bool F32OUT>
-__global__ __launch_bounds__(256) void kv_attention_kernel(
+__global__ __launch_bounds__(256, 2) void kv_attention_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ks,
     const float* __restrict__ kts, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
     const float* __restrict__ vts, void* __restrict__ out, int nq, int tokens, int heads, int frames,
@@ -266,7 +368,6 @@ __global__ __launch_bounds__(256) void kv_attention_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qh = wave & 1, kp = wave >> 1;
   const int c = lane & 31, hf = lane >> 5;
 
   // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
@@ -278,32 +379,31 @@ __global__ __launch_bounds__(256) void kv_attention_kernel(
 
   const int nkeys = frames * tokens;
   const int q0 = qt * kQT;
-  const int qlast = min(q0 + kQT, nq) - 1;
   const int first_frame = frames - q_frames;
-  const int kmin = (first_frame + q0 / tokens + 1) * tokens;      // every query sees keys < kmin
-  const int kmax = (first_frame + qlast / tokens + 1) * tokens;   // no query sees keys >= kmax
+  const int qlast = min(q0 + kQT, nq) - 1;
+  const int kmax = (first_frame + qlast / tokens + 1) * tokens;   // no query of the group sees keys >= kmax
   const int nt = (kmax + kKT - 1) / kKT;
+  // this wavefront's first query sees keys < kmin_w: tiles below need no mask
+  const int qw = min(q0 + 32 * wave, nq - 1);
+  const int kmin_w = (first_frame + qw / tokens + 1) * tokens;
 
-  Geo geo{kc, ks, vc, vs, heads, h, nkeys};
+  Geo geo{kc, ks, vc, vs, heads, h, nkeys, 0u, {0u, 0u, 0u, 0u}};
+  init_geo(geo, tid);
 
-  // Queries of this lane (two columns), converted to fp16 with a per-row
-  // power-of-two scale; d of MFMA step s is 16s + 8hf + j.
-  half8_t qf[2][8];
-  float cq[2];
-  int lim[2];
-  int64_t qrow[2];
-  bool qvalid[2];
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int qi = q0 + 64 * qh + 32 * g + c;
-    qvalid[g] = qi < nq;
-    qrow[g] = (int64_t)qi * heads + h;
-    lim[g] = qvalid[g] ? (first_frame + qi / tokens + 1) * tokens : kmax;
+  // The lane's query, converted to fp16 with a per-row power-of-two scale;
+  // d of MFMA step s is 16s + 8hf + j.
+  const int qi = q0 + 32 * wave + c;
+  const bool qvalid = qi < nq;
+  const int64_t qrow = (int64_t)qi * heads + h;
+  const int lim = qvalid ? (first_frame + qi / tokens + 1) * tokens : kmax;
+  half8_t qf[8];
+  float cq;
+  {
     u32x4_t raw[8];
     float mx = 0.0f;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      raw[s] = qvalid[g] ? *reinterpret_cast<const u32x4_t*>(q + qrow[g] * kD + 16 * s + 8 * hf) : u32x4_t{0, 0, 0, 0};
+      raw[s] = qvalid ? *reinterpret_cast<const u32x4_t*>(q + qrow * kD + 16 * s + 8 * hf) : u32x4_t{0, 0, 0, 0};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         mx = fmaxf(mx, fabsf(bf16_to_f32(raw[s][j] & 0xFFFFu)));
@@ -318,100 +418,72 @@ __global__ __launch_bounds__(256) void kv_attention_kernel(
       e = min(max(15 - E, -126), 126);  // mx * 2^e in [2^14, 2^15) unless clamped
     }
     const float sc = ldexpf(1.0f, e);
-    cq[g] = ldexpf(kLog2eRsqrtD, -e);
+    cq = ldexpf(kLog2eRsqrtD, -e);
 #pragma unroll
     for (int s = 0; s < 8; ++s)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        qf[g][s][2 * j] = (_Float16)(bf16_to_f32(raw[s][j] & 0xFFFFu) * sc);
-        qf[g][s][2 * j + 1] = (_Float16)(bf16_to_f32(raw[s][j] >> 16) * sc);
+        qf[s][2 * j] = (_Float16)(bf16_to_f32(raw[s][j] & 0xFFFFu) * sc);
+        qf[s][2 * j + 1] = (_Float16)(bf16_to_f32(raw[s][j] >> 16) * sc);
       }
   }
 
   State st;
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    st.m[g] = kMInit;
-    st.l[g] = 0.0f;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st.acc[g][db][i] = 0.0f;
-  }
+  st.m = kMInit;
+  st.l = 0.0f;
   st.svref = 0.0f;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.acc[db][i] = 0.0f;
 
+  // Prologue: K and V tile 0 and K tile 1 decoded, the scores of tile 0
+  // computed, raw codes of K tile 2 and V tile 1 in flight.
   Raw raw;
-  load_raw(geo, 0, tid, raw);
+  load_raw_k(geo, 0, tid, raw);
+  load_raw_v(geo, 0, tid, raw);
   decode_k(raw, smem, tid);
   decode_v(raw, smem, tid);
-  if (nt > 1) load_raw(geo, kKT, tid, raw);
-  __syncthreads();
-
-  for (int t = 0; t < nt; ++t) {
-    uint8_t* buf = smem + (t & 1) * kBuf;
-    const int kbase = t * kKT + 32 * kp;
-    if (kbase < kmax) {
-      const int fb = kbase / fb_keys;
-      const float skt = kts[fb], svt = vts[fb];
-      float16_t sacc[2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) { sacc[0][i] = 0.0f; sacc[1][i] = 0.0f; }
-      const uint8_t* ka = buf + (32 * kp + c) * kKRow + 16 * hf;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const half8_t a = *reinterpret_cast<const half8_t*>(ka + 32 * s);
-        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[0][s], sacc[0], 0, 0, 0);
-        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[1][s], sacc[1], 0, 0, 0);
-      }
-      const bool masked = kbase + 32 > kmin;
-      half8_t pb[2][2];
-      softmax_col<0>(sacc[0], cq[0] * skt, masked, kbase, hf, lim[0], st, pb[0][0], pb[0][1]);
-      softmax_col<1>(sacc[1], cq[1] * skt, masked, kbase, hf, lim[1], st, pb[1][0], pb[1][1]);
-      if (svt != 0.0f) {
-        if (st.svref == 0.0f) {
-          st.svref = svt;
-        } else if (svt != st.svref) {
-          const float ratio = st.svref / svt;
-#pragma unroll
-          for (int g = 0; g < 2; ++g)
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) st.acc[g][db][i] *= ratio;
-          st.svref = svt;
-        }
-        const uint8_t* va = buf + kKBuf + c * kVRow + 2 * (32 * kp + 8 * hf);
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const half8_t a = *reinterpret_cast<const half8_t*>(va + (32 * db) * kVRow + 32 * u);
-            st.acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[0][u], st.acc[0][db], 0, 0, 0);
-            st.acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[1][u], st.acc[1][db], 0, 0, 0);
-          }
-      }
-    }
-    if (t + 1 < nt) {
-      uint8_t* nbuf = smem + ((t + 1) & 1) * kBuf;
-      decode_k(raw, nbuf, tid);
-      decode_v(raw, nbuf, tid);
-      if (t + 2 < nt) load_raw(geo, (t + 2) * kKT, tid, raw);
-    }
-    __syncthreads();
+  if (nt > 1) {
+    load_raw_k(geo, kKT, tid, raw);
+    decode_k(raw, smem + kBuf, tid);
   }
-
-  // Merge the two key parities: wavefront (qh, kp) finishes column g = kp and
-  // hands column 1 - kp to its partner.  The loop's last barrier freed LDS.
-  float* parts = reinterpret_cast<float*>(smem);
-  constexpr int kPart = 64 * 64 + 3 * 64;   // floats per (qh, g) region
-  if (kp == 0) stash_col<1>(st, parts + (qh * 2 + 1) * kPart, lane);
-  else stash_col<0>(st, parts + (qh * 2 + 0) * kPart, lane);
+  if (nt > 2) load_raw_k(geo, 2 * kKT, tid, raw);
+  if (nt > 1) load_raw_v(geo, kKT, tid, raw);
   __syncthreads();
-  if (kp == 0) finish_col<0, F32OUT>(st, parts + (qh * 2 + 0) * kPart, lane, qrow[0], qvalid[0], out);
-  else finish_col<1, F32OUT>(st, parts + (qh * 2 + 1) * kPart, lane, qrow[1], qvalid[1], out);
-}
+  float16_t scur[2];
+  qk_tile(smem, c, hf, qf, scur);
+  __syncthreads();   // K tile 0 is read: its buffer is rewritten in the first iteration
 
-static_assert(4 * (64 * 64 + 3 * 64) * 4 <= kLds, "merge regions must fit in LDS");
+  // Tiles wholly below this wavefront's first query limit need no mask; the
+  // two kinds run in two loops (one copy of the tile code each).
+  const Ctx cx{smem, nt, c, hf, tid, lim, fb_keys, cq, kts, vts};
+  const int nt_plain = min(kmin_w / kKT, nt);
+  int t = 0;
+  for (; t < nt_plain; ++t) step<false>(cx, t, qf, geo, raw, scur, st);
+  for (; t < nt; ++t) step<true>(cx, t, qf, geo, raw, scur, st);
+
+  const float l = st.l + __shfl_xor(st.l, 32, 64);
+  const float a = st.svref / l;
+  if (!qvalid) return;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = 32 * db + 8 * i4 + 4 * hf;
+      const float v0 = st.acc[db][4 * i4] * a, v1 = st.acc[db][4 * i4 + 1] * a;
+      const float v2 = st.acc[db][4 * i4 + 2] * a, v3 = st.acc[db][4 * i4 + 3] * a;
+      if constexpr (F32OUT) {
+        float4_t wv = {v0, v1, v2, v3};
+        *reinterpret_cast<float4_t*>(static_cast<float*>(out) + qrow * kD + d) = wv;
+      } else {
+        u32x2_t wv;
+        wv[0] = f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16);
+        wv[1] = f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16);
+        *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + qrow * kD + d) = wv;
+      }
+    }
+}
 
 }  // namespace
 

@@ -184,9 +184,11 @@ def test_kv_attention_rejects_bad_arguments(nv):
     assert call(k=_t(nv, 12 * 40 * 2 - 1, 128)) == EINVAL     # cache rows
     assert call(v=_t(nv, 12 * 40 * 2, 64)) == EINVAL          # head_dim mismatch
     assert call(k=_t(nv, 12 * 40 * 2, 64), v=_t(nv, 12 * 40 * 2, 64), d=64) == EUNS
-    # 8-frame blocks of 13 tokens = 104 keys: not 32-key aligned, two blocks
+    # 8-frame blocks of 13 tokens = 104 keys: not 64-key aligned, two blocks
     k13 = _t(nv, 12 * 13 * 2, 128)
     assert call(k=k13, v=k13, tokens=13) == EUNS
+    k4 = _t(nv, 12 * 4 * 2, 128)                               # 8 x 4 = 32 keys per block
+    assert call(k=k4, v=k4, tokens=4) == EUNS
     # a single frame block needs no alignment; zero queries is a no-op
     k13b = _t(nv, 5 * 13 * 2, 128)
     assert call(k=k13b, v=k13b, frames=5, tokens=13, qf=0) == 0
