@@ -84,7 +84,7 @@ def _case(rng, frames, tokens, heads, q_frames, q_std=1.0, k_std=1.0, v_std=1.0)
 CASES = [
     # frames, tokens, heads, q_frames, frame_block
     (12, 40, 3, 3, 8),     # two frame blocks, ragged last key tile, one query tile
-    (12, 100, 2, 3, 8),    # three query tiles, frame boundaries inside tiles
+    (12, 96, 2, 3, 8),     # three query tiles, frame boundaries inside tiles
     (5, 13, 2, 2, 8),      # one frame block, tokens not a multiple of 32
     (1, 7, 1, 1, 8),       # a single frame: every key visible
     (9, 32, 4, 1, 2),      # five frame blocks of 64 keys
