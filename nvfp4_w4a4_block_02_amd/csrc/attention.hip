@@ -31,17 +31,19 @@
 //     rescaled by the ratio when a key block with another frame-block scale
 //     arrives (once per frame-block boundary).
 //
-// Work split.  A workgroup of 4 wavefronts owns 128 queries of one head.
-// Wavefront w takes queries 64*(w&1) .. +63 (two 32-query MFMA columns) and
-// the key block of parity w>>1 in every 64-key tile, so each wavefront runs
-// 16 + 16 MFMAs per tile and the two parities are merged once at the end.
-// Lanes own queries: in the transposed products each lane holds one query
-// column, so the row maximum, row sum and rescales are per-lane scalars and
-// the probabilities feed the second MFMA from the registers they were
-// computed in (the key order inside an MFMA step is permuted to match, see
-// decode_v).  Tiles are double-buffered in LDS: while tile t is consumed, the
-// raw codes of tile t+1 (loaded one iteration earlier) are decoded into the
-// other buffer; one barrier per tile.
+// Work split.  A workgroup of 4 wavefronts owns 128 queries of one head;
+// wavefront w takes queries 32w .. 32w+31 (one 32-query MFMA column) over all
+// keys, so each wavefront runs 16 + 16 MFMAs per 64-key tile.  Two workgroups
+// share a CU, so the two wavefronts on a SIMD come from different workgroups
+// and their MFMA and VALU work interleaves.  Lanes own queries: in the
+// transposed products each lane holds one query column, so the row maximum,
+// row sum and rescales are per-lane scalars and the probabilities feed the
+// second MFMA from the registers they were computed in (the key order inside
+// an MFMA step is permuted to match, see decode_v).  Tiles are double-buffered
+// in LDS and the loop is software-pipelined by one tile on the K side: the
+// scores of tile t+1 are computed while tile t's softmax runs, and tile t's
+// P V product overlaps the decode of the next tiles (raw codes loaded one
+// iteration earlier); one barrier per tile.
 #include <cmath>
 
 #include "device.h"
