@@ -331,33 +331,59 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
   const bool one_domain = (rpd >= rows);
   const bool narrow = nunits <= 0xFFFFFFFFull;  // 32-bit domain division suffices
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-  auto unit = [&](uint64_t u) {
-    const uint64_t d = one_domain ? 0 : narrow ? (uint64_t)((uint32_t)u / (uint32_t)upd) : u / upd;
-    const float S = ts[d];
-    const float sf = e4m3_to_f32(scales[u * E / kBlock]);
+  // Tensor scale of unit u's domain.  A thread's units rise monotonically and
+  // a domain spans millions of units, so the division runs only when u
+  // leaves the cached range.
+  uint64_t dlo = 0, dhi = one_domain ? ~0ull : 0;
+  float S = one_domain ? ts[0] : 0.0f;
+  auto tscale = [&](uint64_t u) {
+    if (u >= dhi) {
+      const uint64_t d = narrow ? (uint64_t)((uint32_t)u / (uint32_t)upd) : u / upd;
+      dlo = d * upd;
+      dhi = dlo + upd;
+      S = ts[d];
+    }
+    return S;
+  };
+  auto load = [&](uint64_t u, uint32_t& w, uint32_t& sb) {
+    if constexpr (OUT == 1) w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(codes) + u);
+    else w = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(codes) + u);
+    sb = scales[u * E / kBlock];
+  };
+  // P = e2m1 * f32(s_b) is exact; one rounding for P * S, then RNE to bf16.
+  auto store = [&](uint64_t u, uint32_t w, uint32_t sb, float St) {
+    const float sf = e4m3_to_f32(sb);
     if constexpr (OUT == 1) {
       float o[8];
-      decode8_f32(__builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(codes) + u), o);
+      decode8_f32(w, o);
       uint32_t p[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) p[q] = f32_to_bf16_rne((o[2 * q] * sf) * S) | (f32_to_bf16_rne((o[2 * q + 1] * sf) * S) << 16);
+      for (int q = 0; q < 4; ++q) {
+        const bf16x2_t v = {(__bf16)((o[2 * q] * sf) * St), (__bf16)((o[2 * q + 1] * sf) * St)};
+        p[q] = __builtin_bit_cast(uint32_t, v);
+      }
       __builtin_nontemporal_store(u32x4_t{p[0], p[1], p[2], p[3]}, reinterpret_cast<u32x4_t*>(out) + u);
     } else {
-      const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(codes) + u);
       const float2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
       const float2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-      __builtin_nontemporal_store(float4_t{(a.x * sf) * S, (a.y * sf) * S, (b.x * sf) * S, (b.y * sf) * S},
+      __builtin_nontemporal_store(float4_t{(a.x * sf) * St, (a.y * sf) * St, (b.x * sf) * St, (b.y * sf) * St},
                                   reinterpret_cast<float4_t*>(out) + u);
     }
   };
   uint64_t u = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
   for (; u + 3 * stride < nunits; u += 4 * stride) {
-    unit(u);
-    unit(u + stride);
-    unit(u + 2 * stride);
-    unit(u + 3 * stride);
+    // the four units' loads first, then their arithmetic and stores
+    uint32_t w[4], sb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) load(u + j * stride, w[j], sb[j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) store(u + j * stride, w[j], sb[j], tscale(u + j * stride));
   }
-  for (; u < nunits; u += stride) unit(u);
+  for (; u < nunits; u += stride) {
+    uint32_t w, sb;
+    load(u, w, sb);
+    store(u, w, sb, tscale(u));
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void reduce_parts_kernel(const float* __restrict__ parts, int nparts,

@@ -30,6 +30,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // E4M3FN byte of a non-negative finite float32, round-to-nearest-even,
 // saturating at 448 (0x7E).  Pure integer logic on the float32 bit pattern for
