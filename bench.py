@@ -20,6 +20,10 @@ Besides the headline value the line carries:
                 launches on the launch stream;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same
                 workload on this host;
+  device_copy   a 256 MiB device-to-device copy (read + write bytes per
+                second): the practical HBM rate that the HBM-bound rows are
+                also quoted against (frac_copy), beside the 8 TB/s datasheet
+                peak (frac_hbm);
   rows          the other rows of the path, each timed back to back the same
                 way: KV codec
                 quantize (core recipe and Four Over Six) and dequantize
@@ -172,9 +176,23 @@ def _time_loop(torch, fn, sets, steps, warmup):
     return _b2b_ms(torch, stream, lambda i: fn(sets[i % len(sets)]), steps)
 
 
-def bench_rows(nv, torch, wl, steps, warmup):
+def copy_rate(torch):
+    """Reference rate for the HBM-bound rows: a 256 MiB device-to-device copy
+    (torch's copy kernel), read + write bytes over its back-to-back time."""
+    src = torch.ones(1 << 26, device="cuda")
+    dst = torch.empty_like(src)
+    ms = _time_loop(torch, lambda s: dst.copy_(src), [None], 10, 3)
+    nbytes = 2 * src.numel() * 4
+    return {"ms": ms, "GB/s": nbytes / ms / 1e6, "frac_hbm": nbytes / ms / 1e6 / HBM_PEAK_GBS, "bytes": nbytes}
+
+
+def bench_rows(nv, torch, wl, steps, warmup, copy_gbs):
     out = {}
     stream = torch.cuda.current_stream()
+
+    def hbm_row(ms, nbytes):
+        gbs = nbytes / ms / 1e6
+        return {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "frac_copy": gbs / copy_gbs, "bytes": nbytes}
     # KV codec: K and V [12, 880, 24, 128] bf16, 8-frame blocks.
     d = wl.kv_cache()
     shape = (12, 880, 24, 128)
@@ -202,15 +220,9 @@ def bench_rows(nv, torch, wl, steps, warmup):
 
     elems = 2 * 12 * 880 * 24 * 128
     kv_bytes = elems * 2 + elems // 2 + elems // 16 + 2 * 2 * 4
-    ms = _time_loop(torch, kvq, kvsets, steps, warmup)
-    out["kv_quant"] = {"ms": ms, "GB/s": kv_bytes / ms / 1e6, "frac_hbm": kv_bytes / ms / 1e6 / HBM_PEAK_GBS,
-                       "bytes": kv_bytes}
-    ms = _time_loop(torch, kvq6, kvsets, steps, warmup)
-    out["kv_quant_4over6"] = {"ms": ms, "GB/s": kv_bytes / ms / 1e6,
-                              "frac_hbm": kv_bytes / ms / 1e6 / HBM_PEAK_GBS, "bytes": kv_bytes}
-    ms = _time_loop(torch, kvd, kvsets, steps, warmup)
-    out["kv_dequant"] = {"ms": ms, "GB/s": kv_bytes / ms / 1e6, "frac_hbm": kv_bytes / ms / 1e6 / HBM_PEAK_GBS,
-                         "bytes": kv_bytes}
+    out["kv_quant"] = hbm_row(_time_loop(torch, kvq, kvsets, steps, warmup), kv_bytes)
+    out["kv_quant_4over6"] = hbm_row(_time_loop(torch, kvq6, kvsets, steps, warmup), kv_bytes)
+    out["kv_dequant"] = hbm_row(_time_loop(torch, kvd, kvsets, steps, warmup), kv_bytes)
     del kvsets
     # RHT16 + quantize along dim 0, and the weight-gradient GEMM.
     d = wl.rht_wgrad()
@@ -230,9 +242,7 @@ def bench_rows(nv, torch, wl, steps, warmup):
         nv.gemm(s["gq"], s["xq"], out=s["c"], stream=stream)
 
     rbytes = rows * cols * 2 + rows * cols // 2 + rows * cols // 16 + 4
-    ms = _time_loop(torch, rq, rsets, steps, warmup)
-    out["rht16_quantize"] = {"ms": ms, "GB/s": rbytes / ms / 1e6, "frac_hbm": rbytes / ms / 1e6 / HBM_PEAK_GBS,
-                             "bytes": rbytes}
+    out["rht16_quantize"] = hbm_row(_time_loop(torch, rq, rsets, steps, warmup), rbytes)
     ms = _time_loop(torch, wg, rsets, max(steps // 2, 5), 3)
     fl = 2.0 * cols * cols * rows
     out["wgrad_gemm"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_f16_peak": fl / ms / 1e9 / PEAK_TFLOPS["f16"]}
@@ -350,6 +360,7 @@ def main():
 
     torch.cuda.init()
     r = bench_attn_proj(nv, torch, wl, a.steps, a.warmup, a.sets)
+    copy = copy_rate(torch)
     tf = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
     gemm_tf = r["flops"] / (r["gemm_ms"] * 1e-3) / 1e12
     line = {
@@ -375,10 +386,12 @@ def main():
                      "frac_fp8_peak": round(gemm_tf / PEAK_TFLOPS["fp8"], 4),
                      "frac_fp4_peak": round(gemm_tf / PEAK_TFLOPS["fp4"], 4)},
         "act_quant": {"ms": round(r["quant_ms"], 5), "GB/s": round(r["quant_bytes"] / r["quant_ms"] / 1e6, 1),
-                      "frac_hbm": round(r["quant_bytes"] / r["quant_ms"] / 1e6 / HBM_PEAK_GBS, 4)},
+                      "frac_hbm": round(r["quant_bytes"] / r["quant_ms"] / 1e6 / HBM_PEAK_GBS, 4),
+                      "frac_copy": round(r["quant_bytes"] / r["quant_ms"] / 1e6 / copy["GB/s"], 4)},
+        "device_copy": {k: (round(v, 5) if isinstance(v, float) else v) for k, v in copy.items()},
     }
     if not a.no_rows:
-        rows = bench_rows(nv, torch, wl, max(a.steps // 2, 5), max(a.warmup // 2, 2))
+        rows = bench_rows(nv, torch, wl, max(a.steps // 2, 5), max(a.warmup // 2, 2), copy["GB/s"])
         line["rows"] = {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                         for k, v in rows.items()}
     if not a.no_cpu:
