@@ -30,7 +30,9 @@
 // consuming lanes read it (fragment, 16-byte half, lane), so the ds_reads are
 // contiguous and conflict-free.  One barrier per K-tile; the loads of tile
 // t+3 are spread over the MFMA steps of tile t, and the decode of step s+1 is
-// interleaved with the MFMAs of step s.
+// interleaved with the MFMAs of step s.  bf16 outputs of whole wavefront
+// sub-tiles leave through the (then free) LDS ring, transposed into rows, as
+// 16-byte stores; the tensor scales are read during the first tile's wait.
 //
 // Fallback kernel (any K % 16 == 0): the same fragments loaded straight into
 // registers with bounds checks; code bytes past K read as 0.
@@ -47,6 +49,7 @@ typedef __attribute__((address_space(3))) void lvoid_t;
 
 constexpr int kKT = 128;    // K elements per tile
 constexpr int kStages = 3;  // LDS ring depth
+constexpr int kOutRegion = 20736;  // LDS bytes per wavefront for the staged bf16 epilogue
 
 __device__ __forceinline__ half8_t decode8(uint32_t codes, half2_t sig2) {
   half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * sig2;
@@ -170,6 +173,7 @@ __device__ __forceinline__ void store_tile(const float16_t (&acc)[FA][FB], float
   }
 }
 
+
 // Workgroup -> output tile.  Workgroups are dealt round-robin to the 8 XCDs,
 // each with its own L2.  Tiles are put in "band" order (bands of `band` tile
 // columns, row-major inside a band) and every XCD gets one contiguous run of
@@ -285,6 +289,63 @@ __device__ __forceinline__ void read_stage(Frags<FA, FB>& fr, const uint8_t* st,
   }
 }
 
+// bf16 epilogue through LDS for a wavefront's whole (32 FA) x (32 FB)
+// sub-tile inside C: the accumulators are scaled (optionally GELU'd), rounded
+// to bf16 and written to the wavefront's LDS region in row-major order, then
+// read back 16 bytes per lane and stored row-contiguously, so that every
+// global store writes whole 16-byte pieces of rows (one instruction covers
+// 64 x 16 bytes) instead of one bf16 per lane.  IC fragment rows per pass
+// keep the region within kOutRegion bytes.  The row pitch is padded by 16
+// bytes so that the two row groups a 2-byte LDS store touches (rows r and
+// r + 4) fall in different banks.
+template <int FA, int FB, int EPI>
+__device__ __forceinline__ void store_tile_staged(const float16_t (&acc)[FA][FB], float sab, int m0, int n0, int l,
+                                                  int li, int hh, uint8_t* lds, uint16_t* __restrict__ c,
+                                                  int64_t ldc, float* __restrict__ amax_out) {
+  constexpr int COLS = 32 * FB, PITCH = 2 * COLS + 16;
+  constexpr int IC = (FA * 32 * PITCH <= kOutRegion) ? FA : 2;  // fragment rows per pass
+  static_assert(FA % IC == 0 && IC * 32 * PITCH <= kOutRegion, "staging region");
+  constexpr int LPR = COLS / 8;   // lanes per row (16 bytes each)
+  constexpr int RPI = 64 / LPR;   // rows per read instruction
+  static_assert(64 % LPR == 0 && (IC * 32) % RPI == 0, "whole rows per read instruction");
+  float mx = 0.0f;
+#pragma unroll
+  for (int i0 = 0; i0 < FA; i0 += IC) {
+#pragma unroll
+    for (int i = i0; i < i0 + IC; ++i) {
+#pragma unroll
+      for (int j = 0; j < FB; ++j) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * (i - i0) + (r >> 2) * 8 + hh * 4 + (r & 3);
+          float v = acc[i][j][r] * sab;
+          if constexpr (EPI == 1) v = gelu_tanh(v);
+          const uint32_t hb = f32_to_bf16_rne(v);
+          mx = fmaxf(mx, fabsf(bf16_to_f32(hb)));
+          *reinterpret_cast<uint16_t*>(lds + row * PITCH + 2 * (32 * j + li)) = (uint16_t)hb;
+        }
+      }
+    }
+    wait_lgkmcnt0();
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int it = 0; it < IC * 32 / RPI; ++it) {
+      const int row = it * RPI + l / LPR, seg = l % LPR;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + row * PITCH + 16 * seg);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(c + (int64_t)(m0 + 32 * i0 + row) * ldc + n0 + 8 * seg));
+    }
+    if (i0 + IC < FA) {
+      wait_lgkmcnt0();
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  if (amax_out != nullptr) {
+    mx = wave_max(mx);
+    if ((threadIdx.x & 63) == 0 && mx > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(amax_out), __float_as_uint(mx));
+  }
+}
+
+
 // The ring holds three K-tiles.  Every tile body issues exactly L loads
 // (this wave's share of one future tile), so the wait for "tile t+1 landed"
 // is always vmcnt(L), with no branch on the tile index: near the end of K the
@@ -368,6 +429,10 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
 #pragma unroll
     for (int j = 0; j < L; ++j) load(j, min(t, nt - 1), smem + t * STAGE);
   }
+  // The tensor scales, read now so that their latency hides under the wait
+  // for the first tile instead of delaying the epilogue.
+  float sab = ats[0] * bts[0];
+  asm volatile("" : "+v"(sab));
   wait_vmcnt<2 * L>();  // tile 0 landed (this wave's part)
   __builtin_amdgcn_s_barrier();
 
@@ -430,8 +495,20 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
     compute_tile(fr, acc);
   }
 
-  store_tile<FA, FB, OUT, EPI>(acc, ats[0] * bts[0], mwg + wy * 32 * FA, nwg + wx * 32 * FB, li, hh, M, N, c, ldc,
-                               amax_out);
+  const int m0 = mwg + wy * 32 * FA, n0 = nwg + wx * 32 * FB;
+  if constexpr (OUT == 1 && (FB == 2 || FB == 4)) {
+    // Every wave has finished with the LDS ring (its loads landed, its reads
+    // done) before any wave overwrites it with output.
+    __syncthreads();
+    const bool whole = m0 + 32 * FA <= M && n0 + 32 * FB <= N && ldc % 8 == 0 && ((uintptr_t)c & 15) == 0;
+    static_assert(4 * kOutRegion <= kStages * STAGE, "the staging regions reuse the LDS ring");
+    if (whole) {
+      store_tile_staged<FA, FB, EPI>(acc, sab, m0, n0, l, li, hh, smem + wave * kOutRegion, static_cast<uint16_t*>(c),
+                                     ldc, amax_out);
+      return;
+    }
+  }
+  store_tile<FA, FB, OUT, EPI>(acc, sab, m0, n0, li, hh, M, N, c, ldc, amax_out);
 }
 
 // ---------------------------------------------------------------------------

@@ -81,6 +81,29 @@ def test_gemm_into_strided_output(nv):
     assert np.all(h[:, 90:] == 7.0)  # nothing written past N
 
 
+@pytest.mark.parametrize("width", [312, 301])
+@pytest.mark.parametrize("tiles", [(2, 4), (4, 2), (4, 4)])
+def test_gemm_bf16_into_strided_output(nv, width, tiles):
+    """bf16 output rows `width` elements apart: whole wavefront sub-tiles go
+    through the LDS-staged 16-byte stores when rows are 16-byte aligned
+    (width 312), the per-element stores otherwise (width 301); edge sub-tiles
+    always take the per-element stores.  Nothing is written past N."""
+    log(f"gemm bf16 strided width {width} tiles {tiles}")
+    rng = np.random.default_rng(width + 7 * tiles[0])
+    ga, gb, oa, ob = _operands(nv, rng, 200, 300, 256)
+    fill = torch.tensor(3.0, dtype=torch.bfloat16)
+    big = torch.full((200, width), 3.0, dtype=torch.bfloat16, device="cuda")
+    amax = torch.empty(1, device="cuda")
+    nv.gemm(ga, gb, out=big[:, :300], epilogue=nv.EPI_GELU_TANH, amax_out=amax, tiles=tiles)
+    h = big.float().cpu().numpy().astype(np.float64)
+    cref, bound = oracle.gemm_ref(oa, ob)
+    g = oracle.gelu_tanh(cref)
+    tol = 1.13 * 1e-5 * bound + np.abs(g) * 2.0 ** -8 + 8 * np.spacing(np.abs(g).astype(np.float32)) + 1e-37
+    assert np.all(np.abs(h[:, :300] - g) <= tol)
+    assert np.all(h[:, 300:] == float(fill))  # nothing written past N
+    assert amax.item() == float(np.abs(h[:, :300]).max())
+
+
 @pytest.mark.parametrize("m,n,k", [(64, 128, 256), (100, 70, 528), (256, 512, 3072)])
 def test_gelu_epilogue_and_amax(nv, m, n, k):
     log(f"gemm gelu {m}x{n}x{k}")
