@@ -19,7 +19,14 @@ bool valid_dtype(int dt) { return dt == NVFP4_F32 || dt == NVFP4_BF16; }
 int64_t elem_size(int dt) { return dt == NVFP4_F32 ? 4 : 2; }
 
 // Rows stay 16-byte aligned when ld * elem_size is a multiple of 16.
-bool ld_ok(int64_t ld, int dt) { return (ld * elem_size(dt)) % 16 == 0; }
+bool ld_ok(int64_t ld, int dt) { return ld % (16 / elem_size(dt)) == 0; }
+
+// a * b for non-negative sizes, saturated at INT64_MAX instead of
+// overflowing, so that absurd arguments fail the size limits below.
+int64_t mul_sat(int64_t a, int64_t b) {
+  int64_t r;
+  return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
 
 int from_hip(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP; }
 
@@ -48,8 +55,8 @@ int check_dense_to_q(const void* x, int dt, int64_t rows, int64_t cols, int64_t 
   } else {
     return NVFP4_EINVAL;
   }
-  if ((rows / 16 + 1) * (cols + 1) > kMaxBlocks || rows * (cols / 16 + 1) > kMaxBlocks ||
-      (out->k / 16 + 1) * (out->rows + 1) > kMaxBlocks)
+  if (mul_sat(rows / 16 + 1, cols + 1) > kMaxBlocks || mul_sat(rows, cols / 16 + 1) > kMaxBlocks ||
+      mul_sat(out->k / 16 + 1, out->rows + 1) > kMaxBlocks)
     return NVFP4_EUNSUPPORTED;
   return NVFP4_OK;
 }
@@ -78,11 +85,11 @@ size_t nvfp4_workspace_bytes(int op, int64_t rows, int64_t cols) {
     case NVFP4_OP_QUANTIZE:
     case NVFP4_OP_RHT16:
     case NVFP4_OP_AMAX:
-      return (size_t)per_domain * (op == NVFP4_OP_AMAX ? (size_t)ndomains(rows, cols) : 1u);
+      return (size_t)(op == NVFP4_OP_AMAX ? mul_sat(ndomains(rows, cols), per_domain) : per_domain);
     case NVFP4_OP_GEMM:
       return 0;
     case NVFP4_OP_KV_QUANT:
-      return (size_t)(ndomains(rows, cols) * per_domain);
+      return (size_t)mul_sat(ndomains(rows, cols), per_domain);
     default:
       return 0;
   }
@@ -95,7 +102,7 @@ int nvfp4_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
     return NVFP4_EINVAL;
   if (!ws || !aligned16(ws)) return NVFP4_EINVAL;
   if (ws_bytes < nvfp4_workspace_bytes(NVFP4_OP_AMAX, rows, rows_per_domain)) return NVFP4_EWORKSPACE;
-  if (rows * (cols / 16) >= kMaxBlocks) return NVFP4_EUNSUPPORTED;
+  if (mul_sat(rows, cols / 16) >= kMaxBlocks) return NVFP4_EUNSUPPORTED;
   if (rows == 0) return NVFP4_OK;
   hipStream_t s = (hipStream_t)stream;
   const int64_t nd = ndomains(rows, rows_per_domain);
@@ -193,14 +200,14 @@ static int kv_quant_impl(const void* kv, int64_t frames, int64_t tokens, int64_t
   if (!kv || !aligned16(kv) || frames < 0 || tokens < 0 || heads < 0 || head_dim < 0 || head_dim % 16 != 0 ||
       frame_block <= 0)
     return NVFP4_EINVAL;
-  const int64_t rows = frames * tokens * heads;
+  const int64_t rows = mul_sat(mul_sat(frames, tokens), heads);
+  if (rows == INT64_MAX || mul_sat(rows, head_dim / 16 + 1) >= kMaxBlocks) return NVFP4_EUNSUPPORTED;
   if (!tensor_ok(out) || out->rows != rows || out->k != head_dim) return NVFP4_EINVAL;
   if (!ws || !aligned16(ws)) return NVFP4_EINVAL;
   if (ws_bytes < nvfp4_workspace_bytes(NVFP4_OP_KV_QUANT, frames, frame_block)) return NVFP4_EWORKSPACE;
-  if (rows * (head_dim / 16 + 1) >= kMaxBlocks) return NVFP4_EUNSUPPORTED;
   if (rows == 0 || head_dim == 0) return NVFP4_OK;
   hipStream_t s = (hipStream_t)stream;
-  const int64_t rpd = frame_block * tokens * heads;
+  const int64_t rpd = (frame_block < frames ? frame_block : frames) * tokens * heads;  // <= rows
   float* parts = static_cast<float*>(ws);
   const uint32_t np = nvfp4::amax_parts_rows(rows, head_dim, rpd);
   if (nvfp4::launch_amax_parts_rows(kv, NVFP4_BF16, rows, head_dim, head_dim, rpd, parts, np, false, 0, s) !=
@@ -224,12 +231,12 @@ int nvfp4_kv_dequant(const nvfp4_tensor* in, int64_t frames, int64_t tokens, int
                      int64_t frame_block, void* out, void* stream) {
   if (!tensor_ok(in) || !out || !aligned16(out) || frames < 0 || tokens < 0 || heads < 0 || frame_block <= 0)
     return NVFP4_EINVAL;
-  const int64_t rows = frames * tokens * heads;
+  const int64_t rows = mul_sat(mul_sat(frames, tokens), heads);
+  if (rows == INT64_MAX || mul_sat(rows, head_dim / 16 + 1) >= kMaxBlocks) return NVFP4_EUNSUPPORTED;
   if (in->rows != rows || in->k != head_dim) return NVFP4_EINVAL;
-  if (rows * (head_dim / 16 + 1) >= kMaxBlocks) return NVFP4_EUNSUPPORTED;
   if (rows == 0 || head_dim == 0) return NVFP4_OK;
-  return from_hip(nvfp4::launch_dequant(qout(in), rows, head_dim, frame_block * tokens * heads, out, NVFP4_BF16,
-                                        (hipStream_t)stream));
+  const int64_t rpd = (frame_block < frames ? frame_block : frames) * tokens * heads;  // <= rows
+  return from_hip(nvfp4::launch_dequant(qout(in), rows, head_dim, rpd, out, NVFP4_BF16, (hipStream_t)stream));
 }
 
 int nvfp4_kv_attention(const void* q, int64_t q_frames, const nvfp4_tensor* k, const nvfp4_tensor* v,
@@ -238,18 +245,18 @@ int nvfp4_kv_attention(const void* q, int64_t q_frames, const nvfp4_tensor* k, c
   if (!q || !out || !aligned16(q) || !aligned16(out) || !valid_dtype(out_dtype) || frames < 0 || tokens < 0 ||
       heads < 0 || head_dim < 0 || head_dim % 16 != 0 || frame_block <= 0 || q_frames < 0 || q_frames > frames)
     return NVFP4_EINVAL;
-  const int64_t rows = frames * tokens * heads;
+  const int64_t rows = mul_sat(mul_sat(frames, tokens), heads);
+  // 32-bit offsets: code bytes of the cache and the workgroup count
+  if (mul_sat(rows, 64) >= ((int64_t)1 << 31)) return NVFP4_EUNSUPPORTED;
   if (!tensor_ok(k) || !tensor_ok(v) || k->rows != rows || v->rows != rows || k->k != head_dim ||
       v->k != head_dim)
     return NVFP4_EINVAL;
-  const int64_t nq = q_frames * tokens;
+  const int64_t nq = q_frames * tokens;  // <= rows
   if (nq == 0 || heads == 0) return NVFP4_OK;
   if (head_dim != 128) return NVFP4_EUNSUPPORTED;
-  const int64_t nfb = (frames + frame_block - 1) / frame_block;
-  if (nfb > 1 && (frame_block * tokens) % 64 != 0) return NVFP4_EUNSUPPORTED;
-  // 32-bit offsets: code bytes of the cache and the workgroup count
-  if (rows * 64 >= ((int64_t)1 << 31) || ((nq + 127) / 128) * heads >= ((int64_t)1 << 31))
-    return NVFP4_EUNSUPPORTED;
+  const int64_t nfb = frames / frame_block + (frames % frame_block != 0);
+  if (nfb > 1 && (frame_block * tokens) % 64 != 0) return NVFP4_EUNSUPPORTED;  // frame_block < frames here
+  if (((nq + 127) / 128) * heads >= ((int64_t)1 << 31)) return NVFP4_EUNSUPPORTED;
   return from_hip(nvfp4::launch_kv_attention(static_cast<const uint16_t*>(q), qout(k), qout(v), out,
                                              out_dtype == NVFP4_F32, nq, tokens, heads, frames, q_frames,
                                              frame_block, (hipStream_t)stream));
@@ -258,7 +265,7 @@ int nvfp4_kv_attention(const void* q, int64_t q_frames, const nvfp4_tensor* k, c
 int nvfp4_dequantize(const nvfp4_tensor* in, int64_t rows_per_domain, void* out, int dtype, void* stream) {
   if (!tensor_ok(in) || !out || !aligned16(out) || !valid_dtype(dtype) || rows_per_domain < 0)
     return NVFP4_EINVAL;
-  if (in->rows * (in->k / 16 + 1) >= kMaxBlocks) return NVFP4_EUNSUPPORTED;
+  if (mul_sat(in->rows, in->k / 16 + 1) >= kMaxBlocks) return NVFP4_EUNSUPPORTED;
   if (in->rows == 0 || in->k == 0) return NVFP4_OK;
   return from_hip(nvfp4::launch_dequant(qout(in), in->rows, in->k, rows_per_domain, out, dtype,
                                         (hipStream_t)stream));

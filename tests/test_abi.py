@@ -193,3 +193,25 @@ def test_kv_attention_rejects_bad_arguments(nv):
     k13b = _t(nv, 5 * 13 * 2, 128)
     assert call(k=k13b, v=k13b, frames=5, tokens=13, qf=0) == 0
     assert call(qf=0) == 0
+
+
+def test_absurd_sizes_are_rejected_without_overflow(nv):
+    """Sizes whose products overflow 64 bits are rejected on the host
+    (unsupported size or a shape mismatch), never wrapped into a launch."""
+    W = ctypes.c_void_p(FAKE)
+    huge = 1 << 40
+    ws = ctypes.c_void_p(FAKE)
+    kq = nv.lib.nvfp4_kv_quant
+    assert kq(W, huge, huge, 2, 32, 8, ctypes.byref(_t(nv, 64, 32)), ws, 8192, _stream()) == -2
+    assert kq(W, 2, huge, huge, 32, 8, ctypes.byref(_t(nv, 64, 32)), ws, 8192, _stream()) == -2
+    kd = nv.lib.nvfp4_kv_dequant
+    assert kd(ctypes.byref(_t(nv, 64, 32)), huge, huge, 2, 32, 8, W, _stream()) == -2
+    at = nv.lib.nvfp4_kv_attention
+    k = _t(nv, 64, 128)
+    assert at(W, 1, ctypes.byref(k), ctypes.byref(k), huge, huge, 2, 128, 8, W, 0, _stream()) == -2
+    q = nv.lib.nvfp4_quantize
+    big = (1 << 62) - 16
+    assert q(W, 1, big, big, big, 1, ctypes.byref(_t(nv, big, big)), ws, 4096, _stream()) == -2
+    assert nv.lib.nvfp4_workspace_bytes(nv.OP_KV_QUANT, 1 << 62, 1) >= 1 << 62
+    dq = nv.lib.nvfp4_dequantize
+    assert dq(ctypes.byref(_t(nv, big, big)), 0, W, 0, _stream()) == -2
