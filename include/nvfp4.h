@@ -183,11 +183,11 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtyp
  * nvfp4_gemm with an explicit tile shape instead of the built-in choice.
  * tile_fa x tile_fb is the number of 32x32 MFMA fragments per wavefront
  * along M x N (a workgroup covers 64*tile_fa x 64*tile_fb outputs); the
- * supported shapes are 2x4, 4x2, 3x3 and 4x4, used when K % 128 == 0 (other
- * K always take the bounds-checked 2x4 kernel).  Results are identical in
- * tolerance, not bit-for-bit, across shapes (the fp32 summation order of an
- * output element is the same; only scheduling differs).  Unsupported shapes
- * return NVFP4_EINVAL.  Intended for tuning and testing.
+ * supported shapes are 2x4, 4x2, 3x3 and 4x4, used when K >= 128 and
+ * K % 64 == 0 (other K always take the bounds-checked 2x4 kernel).  Every
+ * shape accumulates each output element in the same order, so results are
+ * bit-identical across shapes.  Unsupported shapes return NVFP4_EINVAL.
+ * Intended for tuning and testing.
  */
 int nvfp4_gemm_tiled(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype,
                      int64_t ldc, int epilogue, float *amax_out, int tile_fa, int tile_fb,

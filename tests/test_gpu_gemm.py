@@ -70,6 +70,26 @@ def test_gemm_every_tile_shape(nv, tiles, m, n, k):
     assert amax.item() == float(np.abs(hh).max())
 
 
+@pytest.mark.parametrize("m,n,k", [(300, 520, 384), (65, 300, 1344), (512, 512, 3072)])
+def test_tile_shapes_are_bit_identical(nv, m, n, k):
+    """Every tile shape (and the automatic choice) accumulates an output
+    element in the same order: float32 results are bit-identical.  The data
+    span a wide range, so the float32 sums do round (checked against the
+    float64 oracle), which makes the identity a property of the order."""
+    log(f"gemm tile-shape identity {m}x{n}x{k}")
+    rng = np.random.default_rng(m * 7 + k)
+    a = (rng.standard_normal((m, k)) * np.exp(rng.uniform(-4, 4, (m, 1)))).astype(np.float32)
+    a[rng.random(a.shape) < 0.02] *= 50
+    b = (rng.standard_normal((n, k)) * np.exp(rng.uniform(-3, 3, (1, k)))).astype(np.float32)
+    ga, gb = nv.quantize(dev_f32(a)), nv.quantize(dev_f32(b))
+    outs = [nv.gemm(ga, gb, out_dtype=torch.float32, tiles=t).cpu().numpy() for t in (None, (2, 4), (4, 2), (3, 3), (4, 4))]
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+    cref, bound = oracle.gemm_ref(oracle.quantize(a), oracle.quantize(b))
+    assert_gemm_close(outs[0], cref, bound, False, "tile identity")
+    assert np.any(outs[0] != cref.astype(np.float32))  # the float32 accumulation rounded somewhere
+
+
 def test_gemm_into_strided_output(nv):
     rng = np.random.default_rng(3)
     ga, gb, oa, ob = _operands(nv, rng, 70, 90, 256)
