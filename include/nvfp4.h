@@ -41,8 +41,11 @@
  *   - Errors: argument problems are detected on the host before any HIP call
  *     and return NVFP4_EINVAL (null pointer, k % 16 != 0, ld < cols,
  *     misalignment, mismatched operands, unknown dtype/flag); a workspace that
- *     is too small returns NVFP4_EWORKSPACE; a failed launch returns
- *     NVFP4_EHIP.  Zero-sized problems return NVFP4_OK without launching.
+ *     is too small returns NVFP4_EWORKSPACE; problems beyond the kernels'
+ *     32-bit indexing (2^31 16-element blocks per tensor; GEMM dimensions of
+ *     2^31 or more) return NVFP4_EUNSUPPORTED, as do shapes whose size
+ *     products overflow 64 bits; a failed launch returns NVFP4_EHIP.
+ *     Zero-sized problems return NVFP4_OK without launching.
  *   - Inputs must be finite.  Non-finite inputs give unspecified codes; there
  *     is no check on the device.  Tensors whose amax is below about 2^-100
  *     (where 1/(s_b * S) overflows float32) also give unspecified codes.
