@@ -25,17 +25,16 @@ Besides the headline value the line carries:
                 also quoted against (frac_copy), beside the 8 TB/s datasheet
                 peak (frac_hbm);
   rows          the other rows of the path, each timed back to back the same
-                way: KV codec
-                quantize (core recipe and Four Over Six) and dequantize
-                (12x880x24x128 bf16, K and V), RHT16 +
-                quantize of a 16384x3072 gradient along dim 0, the 3072x3072x
-                16384 weight-gradient GEMM, the FFN pair
-                (10560x3072 -> 14336 -> 3072), and the NVFP4 training triple
-                (forward, input and weight gradient, with the six operand
-                quantizations) of a 2640x3072x3072 linear layer, and the
+                way, in this order: KV codec quantize (core recipe and Four
+                Over Six) and dequantize (12x880x24x128 bf16, K and V); the
                 frame-causal window attention of 2640 queries (3 latent
-                frames) x 24 heads over the 12-frame NVFP4 KV cache, read
-                directly (flops counted over the visible query-key pairs).
+                frames) x 24 heads over that 12-frame NVFP4 KV cache, read
+                directly (flops counted over the visible query-key pairs);
+                RHT16 + quantize of a 16384x3072 gradient along dim 0 and the
+                3072x3072x16384 weight-gradient GEMM; the FFN pair
+                (10560x3072 -> 14336 -> 3072); the NVFP4 training triple
+                (forward, input and weight gradient, with the six operand
+                quantizations) of a 2640x3072x3072 linear layer.
 """
 
 from __future__ import annotations
@@ -225,6 +224,28 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs):
     out["kv_quant_4over6"] = hbm_row(_time_loop(torch, kvq6, kvsets, steps, warmup), kv_bytes)
     out["kv_dequant"] = hbm_row(_time_loop(torch, kvd, kvsets, steps, warmup), kv_bytes)
     del kvsets
+    # Window attention reading the NVFP4 KV cache directly: the chunk's 3
+    # latent frames of queries against the 12-frame cache (frame-causal).
+    d = wl.window_attention()
+    fr, tk, hd, dd = 12, 880, 24, 128
+    asets = []
+    for i in range(3):
+        kk = _dev_bf16(torch, d["k"]).reshape(fr, tk, hd, dd)
+        vv = _dev_bf16(torch, d["v"]).reshape(fr, tk, hd, dd)
+        s = {"q": _dev_bf16(torch, d["q"]).reshape(3 * tk, hd, dd), "k": nv.kv_quant(kk), "v": nv.kv_quant(vv)}
+        s["o"] = torch.empty_like(s["q"])
+        asets.append(s)
+        del kk, vv
+
+    def attn(s):
+        nv.kv_attention(s["q"], s["k"], s["v"], (fr, tk, hd, dd), 8, out=s["o"], stream=stream)
+
+    ms = _time_loop(torch, attn, asets, max(steps // 2, 5), 2)
+    pairs = sum((fr - 3 + f + 1) * tk for f in range(3)) * tk      # visible (query, key) pairs per head
+    fl = 4.0 * pairs * dd * hd
+    out["kv_window_attention"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9,
+                                  "frac_f16_peak": fl / ms / 1e9 / PEAK_TFLOPS["f16"]}
+    del asets
     # RHT16 + quantize along dim 0, and the weight-gradient GEMM.
     d = wl.rht_wgrad()
     rows, cols = d["g"].shape
@@ -292,27 +313,6 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs):
     fl = 3 * 2.0 * m * n * k
     out["train_linear_triple"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_f16_peak": fl / ms / 1e9 / PEAK_TFLOPS["f16"]}
     del tsets
-    # Window attention reading the NVFP4 KV cache directly: the chunk's 3
-    # latent frames of queries against the 12-frame cache (frame-causal).
-    d = wl.window_attention()
-    fr, tk, hd, dd = 12, 880, 24, 128
-    asets = []
-    for i in range(3):
-        kk = _dev_bf16(torch, d["k"]).reshape(fr, tk, hd, dd)
-        vv = _dev_bf16(torch, d["v"]).reshape(fr, tk, hd, dd)
-        s = {"q": _dev_bf16(torch, d["q"]).reshape(3 * tk, hd, dd), "k": nv.kv_quant(kk), "v": nv.kv_quant(vv)}
-        s["o"] = torch.empty_like(s["q"])
-        asets.append(s)
-        del kk, vv
-
-    def attn(s):
-        nv.kv_attention(s["q"], s["k"], s["v"], (fr, tk, hd, dd), 8, out=s["o"], stream=stream)
-
-    ms = _time_loop(torch, attn, asets, max(steps // 2, 5), 2)
-    pairs = sum((fr - 3 + f + 1) * tk for f in range(3)) * tk      # visible (query, key) pairs per head
-    fl = 4.0 * pairs * dd * hd
-    out["kv_window_attention"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9,
-                                  "frac_f16_peak": fl / ms / 1e9 / PEAK_TFLOPS["f16"]}
     return out
 
 
