@@ -25,7 +25,8 @@ Besides the headline value the line carries:
                 also quoted against (frac_copy), beside the 8 TB/s datasheet
                 peak (frac_hbm);
   rows          the other rows of the path, each timed back to back the same
-                way, in this order: KV codec quantize (core recipe and Four
+                way in five batches (ms = mean over all calls; ms_median and
+                ms_min of the batch means), in this order: KV codec quantize (core recipe and Four
                 Over Six) and dequantize (12x880x24x128 bf16, K and V); the
                 frame-causal window attention of 2640 queries (3 latent
                 frames) x 24 heads over that 12-frame NVFP4 KV cache, read
@@ -166,14 +167,25 @@ def bench_attn_proj(nv, torch, wl, steps, warmup, nsets):
     }
 
 
-def _time_loop(torch, fn, sets, steps, warmup):
-    """Mean time of one call of `fn(set)` over `steps` back-to-back calls that
-    rotate through `sets` (after `warmup` untimed calls)."""
+def _time_loop(torch, fn, sets, steps, warmup, batches=5):
+    """Time of one call of `fn(set)` over `steps` back-to-back calls that
+    rotate through `sets` (after `warmup` untimed calls), run as up to
+    `batches` back-to-back batches with one event pair each.  Returns the
+    mean over all calls ("ms") and the median and minimum of the batch means
+    ("ms_median", "ms_min")."""
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         fn(sets[i % len(sets)])
     torch.cuda.synchronize()
-    return _b2b_ms(torch, stream, lambda i: fn(sets[i % len(sets)]), steps)
+    nb = max(1, min(batches, steps))
+    means, total, i0 = [], 0.0, 0
+    for b in range(nb):
+        size = steps // nb + (1 if b < steps % nb else 0)
+        ms = _b2b_ms(torch, stream, lambda i, i0=i0: fn(sets[(i0 + i) % len(sets)]), size)
+        means.append(ms)
+        total += ms * size
+        i0 += size
+    return {"ms": total / steps, "ms_median": float(np.median(means)), "ms_min": float(min(means))}
 
 
 def copy_rate(torch):
@@ -181,7 +193,7 @@ def copy_rate(torch):
     (torch's copy kernel), read + write bytes over its back-to-back time."""
     src = torch.ones(1 << 26, device="cuda")
     dst = torch.empty_like(src)
-    ms = _time_loop(torch, lambda s: dst.copy_(src), [None], 10, 3)
+    ms = _time_loop(torch, lambda s: dst.copy_(src), [None], 10, 3)["ms"]
     nbytes = 2 * src.numel() * 4
     return {"ms": ms, "GB/s": nbytes / ms / 1e6, "frac_hbm": nbytes / ms / 1e6 / HBM_PEAK_GBS, "bytes": nbytes}
 
@@ -190,9 +202,13 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs):
     out = {}
     stream = torch.cuda.current_stream()
 
-    def hbm_row(ms, nbytes):
-        gbs = nbytes / ms / 1e6
-        return {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "frac_copy": gbs / copy_gbs, "bytes": nbytes}
+    def hbm_row(t, nbytes):
+        gbs = nbytes / t["ms"] / 1e6
+        return {**t, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "frac_copy": gbs / copy_gbs, "bytes": nbytes}
+
+    def flop_row(t, flops):
+        tf = flops / t["ms"] / 1e9
+        return {**t, "TFLOP/s": tf, "frac_f16_peak": tf / PEAK_TFLOPS["f16"]}
     # KV codec: K and V [12, 880, 24, 128] bf16, 8-frame blocks.
     d = wl.kv_cache()
     shape = (12, 880, 24, 128)
@@ -240,11 +256,9 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs):
     def attn(s):
         nv.kv_attention(s["q"], s["k"], s["v"], (fr, tk, hd, dd), 8, out=s["o"], stream=stream)
 
-    ms = _time_loop(torch, attn, asets, max(steps // 2, 5), 2)
     pairs = sum((fr - 3 + f + 1) * tk for f in range(3)) * tk      # visible (query, key) pairs per head
-    fl = 4.0 * pairs * dd * hd
-    out["kv_window_attention"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9,
-                                  "frac_f16_peak": fl / ms / 1e9 / PEAK_TFLOPS["f16"]}
+    out["kv_window_attention"] = flop_row(_time_loop(torch, attn, asets, max(steps // 2, 5), 2),
+                                          4.0 * pairs * dd * hd)
     del asets
     # RHT16 + quantize along dim 0, and the weight-gradient GEMM.
     d = wl.rht_wgrad()
@@ -265,9 +279,7 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs):
 
     rbytes = rows * cols * 2 + rows * cols // 2 + rows * cols // 16 + 4
     out["rht16_quantize"] = hbm_row(_time_loop(torch, rq, rsets, steps, warmup), rbytes)
-    ms = _time_loop(torch, wg, rsets, max(steps // 2, 5), 3)
-    fl = 2.0 * cols * cols * rows
-    out["wgrad_gemm"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_f16_peak": fl / ms / 1e9 / PEAK_TFLOPS["f16"]}
+    out["wgrad_gemm"] = flop_row(_time_loop(torch, wg, rsets, max(steps // 2, 5), 3), 2.0 * cols * cols * rows)
     del rsets
     # FFN pair.
     d = wl.ffn()
@@ -284,9 +296,7 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs):
     def ffn(s):
         nv.ffn(x, w1, w2, bufs=bufs, stream=stream)
 
-    ms = _time_loop(torch, ffn, [None], max(steps // 5, 3), 2)
-    fl = 2.0 * m * dm * f * 2
-    out["ffn_pair"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_f16_peak": fl / ms / 1e9 / PEAK_TFLOPS["f16"]}
+    out["ffn_pair"] = flop_row(_time_loop(torch, ffn, [None], max(steps // 5, 3), 2), 2.0 * m * dm * f * 2)
     del bufs, x, w1, w2
     # Training triple of one linear layer at the attention-projection shape:
     # six quantizations (two with the RHT16) and three GEMMs per step.
@@ -309,9 +319,7 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs):
     def train(s):
         nv.linear_train(s["x"], s["w"], s["dy"], d["mask"], bufs=s["bufs"], stream=stream)
 
-    ms = _time_loop(torch, train, tsets, max(steps // 2, 5), 2)
-    fl = 3 * 2.0 * m * n * k
-    out["train_linear_triple"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_f16_peak": fl / ms / 1e9 / PEAK_TFLOPS["f16"]}
+    out["train_linear_triple"] = flop_row(_time_loop(torch, train, tsets, max(steps // 2, 5), 2), 3 * 2.0 * m * n * k)
     del tsets
     return out
 
