@@ -108,6 +108,29 @@ def _ptr(t: torch.Tensor | None):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+def _on_gpu(t: torch.Tensor, name: str):
+    """The C ABI takes device pointers: a host tensor handed to a kernel would
+    fault the GPU, so it is refused here."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+
+
+def _need(t: torch.Tensor, name: str, shape=None, dtype=None, min_numel: int = 0, gpu: bool = True):
+    """An output or auxiliary buffer the kernels write or read in full: right
+    dtype, contiguous, of the required shape or size, and (unless `gpu` is
+    False, for a caller that checks the device last) on the GPU."""
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} needs at least {min_numel} elements, has {t.numel()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if gpu:
+        _on_gpu(t, name)
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return F32
@@ -133,7 +156,18 @@ class NVFP4Tensor:
     def k(self) -> int:
         return self.codes.shape[1] * 2
 
-    def c(self) -> _CTensor:
+    def c(self, n_domains: int = 1) -> _CTensor:
+        """The C view; checks first that the three buffers match each other
+        (codes [rows, k/2] and scales [rows, k/16] uint8, at least
+        `n_domains` float32 tensor scales), so that no kernel reads or writes
+        past them."""
+        if self.codes.dim() != 2:
+            raise ValueError("codes must be 2-D [rows, k/2]")
+        _need(self.codes, "codes", dtype=torch.uint8, gpu=False)
+        _need(self.scales, "scales", shape=(self.rows, self.k // 16), dtype=torch.uint8, gpu=False)
+        _need(self.tscale, "tscale", dtype=torch.float32, min_numel=max(n_domains, 1), gpu=False)
+        for name, t in (("codes", self.codes), ("scales", self.scales), ("tscale", self.tscale)):
+            _on_gpu(t, name)
         return _CTensor(self.codes.data_ptr(), self.scales.data_ptr(), self.tscale.data_ptr(), self.rows, self.k)
 
     @staticmethod
@@ -155,8 +189,9 @@ def _workspace(op, rows, cols, device):
 
 
 def _ld(x: torch.Tensor) -> int:
-    """Leading dimension of a row-major 2-D tensor (a single row may carry any
-    stride in torch; it is then reported as the row length)."""
+    """Leading dimension of a row-major 2-D tensor on the GPU (a single row may
+    carry any stride in torch; it is then reported as the row length)."""
+    _on_gpu(x, "tensor")
     if x.dim() != 2:
         raise ValueError("expected a 2-D tensor")
     if x.shape[1] > 1 and x.stride(1) != 1:
@@ -175,8 +210,10 @@ def amax(x: torch.Tensor, rows_per_domain: int = 0, out: torch.Tensor | None = N
     nd = 1 if rows_per_domain <= 0 or rows_per_domain >= rows else -(-rows // rows_per_domain)
     if out is None:
         out = torch.empty((nd,), dtype=torch.float32, device=x.device)
+    _need(out, "out", dtype=torch.float32, min_numel=nd)
     if ws is None:
         ws = _workspace(OP_AMAX, rows, rows_per_domain, x.device)
+    _need(ws, "ws")
     _check(_lib().nvfp4_amax(_ptr(x), _dtype_code(x), rows, cols, _ld(x), rows_per_domain, _ptr(out),
                           _ptr(ws), ws.numel() * 4, _stream(stream)), "nvfp4_amax")
     return out
@@ -185,10 +222,12 @@ def amax(x: torch.Tensor, rows_per_domain: int = 0, out: torch.Tensor | None = N
 def encode(x: torch.Tensor, amax_t: torch.Tensor, axis: int = 1, rows_per_domain: int = 0,
            out: NVFP4Tensor | None = None, stream=None) -> NVFP4Tensor:
     rows, cols = x.shape
+    nd = 1 if rows_per_domain <= 0 or rows_per_domain >= rows else -(-rows // rows_per_domain)
+    _need(amax_t, "amax", dtype=torch.float32, min_numel=nd)
     if out is None:
         r, k = _out_shape(x, axis)
-        out = NVFP4Tensor.empty(r, k, amax_t.numel(), x.device)
-    ct = out.c()
+        out = NVFP4Tensor.empty(r, k, nd, x.device)
+    ct = out.c(nd)
     _check(_lib().nvfp4_encode(_ptr(x), _dtype_code(x), rows, cols, _ld(x), axis, rows_per_domain,
                             _ptr(amax_t), ctypes.byref(ct), _stream(stream)), "nvfp4_encode")
     return out
@@ -202,6 +241,7 @@ def quantize(x: torch.Tensor, axis: int = 1, out: NVFP4Tensor | None = None, ws:
         out = NVFP4Tensor.empty(r, k, 1, x.device)
     if ws is None:
         ws = _workspace(OP_QUANTIZE, rows, cols, x.device)
+    _need(ws, "ws")
     ct = out.c()
     _check(_lib().nvfp4_quantize(_ptr(x), _dtype_code(x), rows, cols, _ld(x), axis, ctypes.byref(ct),
                               _ptr(ws), ws.numel() * 4, _stream(stream)), "nvfp4_quantize")
@@ -218,6 +258,7 @@ def rht16_quantize(x: torch.Tensor, sign_mask: int, axis: int = 1, out: NVFP4Ten
         out = NVFP4Tensor.empty(r, max(k, k_pad) if axis == 0 else k, 1, x.device)
     if ws is None:
         ws = _workspace(OP_RHT16, rows, cols, x.device)
+    _need(ws, "ws")
     ct = out.c()
     _check(_lib().rht16_quantize(_ptr(x), _dtype_code(x), rows, cols, _ld(x), axis, sign_mask,
                               ctypes.byref(ct), _ptr(ws), ws.numel() * 4, _stream(stream)), "rht16_quantize")
@@ -231,6 +272,10 @@ def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.bfloat16, epilogue: int
     (fragments along M, fragments along N) per wavefront; default: automatic."""
     if out is None:
         out = torch.empty((a.rows, b.rows), dtype=out_dtype, device=a.codes.device)
+    if tuple(out.shape) != (a.rows, b.rows):
+        raise ValueError(f"out must have shape {(a.rows, b.rows)}, got {tuple(out.shape)}")
+    if amax_out is not None:
+        _need(amax_out, "amax_out", dtype=torch.float32, min_numel=1)
     ca, cb = a.c(), b.c()
     if tiles is None:
         _check(_lib().nvfp4_gemm(ctypes.byref(ca), ctypes.byref(cb), _ptr(out), _dtype_code(out), _ld(out),
@@ -249,12 +294,14 @@ def kv_quant(kv: torch.Tensor, frame_block: int = 8, out: NVFP4Tensor | None = N
     f, t, h, d = kv.shape
     if kv.dtype != torch.bfloat16 or not kv.is_contiguous():
         raise TypeError("kv must be a contiguous bfloat16 tensor [frames, tokens, heads, head_dim]")
-    nd = -(-f // frame_block)
+    _on_gpu(kv, "kv")
+    nd = -(-f // frame_block) if frame_block > 0 else 1
     if out is None:
         out = NVFP4Tensor.empty(f * t * h, d, nd, kv.device)
     if ws is None:
         ws = _workspace(OP_KV_QUANT, f, frame_block, kv.device)
-    ct = out.c()
+    _need(ws, "ws")
+    ct = out.c(nd)
     fn = _lib().nvfp4_kv_quant_4over6 if four_over_six else _lib().nvfp4_kv_quant
     _check(fn(_ptr(kv), f, t, h, d, frame_block, ctypes.byref(ct), _ptr(ws), ws.numel() * 4, _stream(stream)),
            "nvfp4_kv_quant_4over6" if four_over_six else "nvfp4_kv_quant")
@@ -266,7 +313,8 @@ def kv_dequant(q: NVFP4Tensor, shape, frame_block: int = 8, out: torch.Tensor | 
     f, t, h, d = shape
     if out is None:
         out = torch.empty((f, t, h, d), dtype=torch.bfloat16, device=q.codes.device)
-    ct = q.c()
+    _need(out, "out", shape=(f, t, h, d), dtype=torch.bfloat16)
+    ct = q.c(-(-f // frame_block) if frame_block > 0 else 1)
     _check(_lib().nvfp4_kv_dequant(ctypes.byref(ct), f, t, h, d, frame_block, _ptr(out), _stream(stream)),
            "nvfp4_kv_dequant")
     return out
@@ -281,10 +329,13 @@ def kv_attention(q: torch.Tensor, k: NVFP4Tensor, v: NVFP4Tensor, shape, frame_b
     if q.dtype != torch.bfloat16 or not q.is_contiguous() or q.dim() != 3 or q.shape[1:] != (h, d) \
             or t == 0 or q.shape[0] % t:
         raise TypeError("q must be a contiguous bfloat16 tensor [q_frames * tokens, heads, head_dim]")
+    _on_gpu(q, "q")
     qf = q.shape[0] // t
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
-    ck, cv = k.c(), v.c()
+    _need(out, "out", shape=q.shape)
+    nfb = -(-f // frame_block) if frame_block > 0 else 1
+    ck, cv = k.c(nfb), v.c(nfb)
     _check(_lib().nvfp4_kv_attention(_ptr(q), qf, ctypes.byref(ck), ctypes.byref(cv), f, t, h, d, frame_block,
                                      _ptr(out), _dtype_code(out), _stream(stream)), "nvfp4_kv_attention")
     return out
@@ -294,7 +345,9 @@ def dequantize(q: NVFP4Tensor, dtype=torch.float32, rows_per_domain: int = 0, ou
                stream=None) -> torch.Tensor:
     if out is None:
         out = torch.empty((q.rows, q.k), dtype=dtype, device=q.codes.device)
-    ct = q.c()
+    _need(out, "out", shape=(q.rows, q.k))
+    nd = 1 if rows_per_domain <= 0 or rows_per_domain >= q.rows else -(-q.rows // rows_per_domain)
+    ct = q.c(nd)
     _check(_lib().nvfp4_dequantize(ctypes.byref(ct), rows_per_domain, _ptr(out), _dtype_code(out), _stream(stream)),
            "nvfp4_dequantize")
     return out

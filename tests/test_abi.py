@@ -7,6 +7,7 @@ import os
 import re
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -215,3 +216,28 @@ def test_absurd_sizes_are_rejected_without_overflow(nv):
     assert nv.lib.nvfp4_workspace_bytes(nv.OP_KV_QUANT, 1 << 62, 1) >= 1 << 62
     dq = nv.lib.nvfp4_dequantize
     assert dq(ctypes.byref(_t(nv, big, big)), 0, W, 0, _stream()) == -2
+
+
+def test_binding_refuses_host_tensors_and_mismatched_buffers(nv):
+    """The binding checks tensors before any C-ABI call: a host tensor (whose
+    pointer a kernel would dereference on the GPU) and NVFP4 buffers that do
+    not match each other are refused with an exception (CPU-only test)."""
+    x = torch.zeros((4, 32), dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="CUDA"):
+        nv.quantize(x)
+    with pytest.raises(TypeError, match="CUDA"):
+        nv.amax(x)
+    good = nv.NVFP4Tensor(torch.zeros((4, 16), dtype=torch.uint8), torch.zeros((4, 2), dtype=torch.uint8),
+                          torch.zeros((1,), dtype=torch.float32))
+    with pytest.raises(TypeError, match="CUDA"):
+        good.c()
+    short_scales = nv.NVFP4Tensor(good.codes, torch.zeros((4, 1), dtype=torch.uint8), good.tscale)
+    with pytest.raises(ValueError, match="scales"):
+        short_scales.c()
+    with pytest.raises(ValueError, match="tscale"):
+        good.c(n_domains=2)
+    wrong_dtype = nv.NVFP4Tensor(good.codes, good.scales, torch.zeros((1,), dtype=torch.float16))
+    with pytest.raises(TypeError, match="tscale"):
+        wrong_dtype.c()
+    with pytest.raises(ValueError, match="out must have shape"):
+        nv.gemm(good, good, out=torch.zeros((3, 4)))
