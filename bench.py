@@ -199,6 +199,9 @@ def copy_rate(torch):
 
 
 def bench_rows(nv, torch, wl, steps, warmup, copy_gbs):
+    """Every row gets ~10 ms or more of untimed warmup calls: the GPU's clocks
+    take milliseconds to settle after a change of load (the window attention
+    measured ~500 us right after the KV codec rows and ~430 us once settled)."""
     out = {}
     stream = torch.cuda.current_stream()
 
@@ -257,7 +260,7 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs):
         nv.kv_attention(s["q"], s["k"], s["v"], (fr, tk, hd, dd), 8, out=s["o"], stream=stream)
 
     pairs = sum((fr - 3 + f + 1) * tk for f in range(3)) * tk      # visible (query, key) pairs per head
-    out["kv_window_attention"] = flop_row(_time_loop(torch, attn, asets, max(steps // 2, 5), 2),
+    out["kv_window_attention"] = flop_row(_time_loop(torch, attn, asets, max(steps // 2, 5), 20),
                                           4.0 * pairs * dd * hd)
     del asets
     # RHT16 + quantize along dim 0, and the weight-gradient GEMM.
@@ -279,7 +282,7 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs):
 
     rbytes = rows * cols * 2 + rows * cols // 2 + rows * cols // 16 + 4
     out["rht16_quantize"] = hbm_row(_time_loop(torch, rq, rsets, steps, warmup), rbytes)
-    out["wgrad_gemm"] = flop_row(_time_loop(torch, wg, rsets, max(steps // 2, 5), 3), 2.0 * cols * cols * rows)
+    out["wgrad_gemm"] = flop_row(_time_loop(torch, wg, rsets, max(steps // 2, 5), 20), 2.0 * cols * cols * rows)
     del rsets
     # FFN pair.
     d = wl.ffn()
@@ -296,7 +299,7 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs):
     def ffn(s):
         nv.ffn(x, w1, w2, bufs=bufs, stream=stream)
 
-    out["ffn_pair"] = flop_row(_time_loop(torch, ffn, [None], max(steps // 5, 3), 2), 2.0 * m * dm * f * 2)
+    out["ffn_pair"] = flop_row(_time_loop(torch, ffn, [None], max(steps // 5, 3), 5), 2.0 * m * dm * f * 2)
     del bufs, x, w1, w2
     # Training triple of one linear layer at the attention-projection shape:
     # six quantizations (two with the RHT16) and three GEMMs per step.
@@ -319,7 +322,7 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs):
     def train(s):
         nv.linear_train(s["x"], s["w"], s["dy"], d["mask"], bufs=s["bufs"], stream=stream)
 
-    out["train_linear_triple"] = flop_row(_time_loop(torch, train, tsets, max(steps // 2, 5), 2), 3 * 2.0 * m * n * k)
+    out["train_linear_triple"] = flop_row(_time_loop(torch, train, tsets, max(steps // 2, 5), 30), 3 * 2.0 * m * n * k)
     del tsets
     return out
 
