@@ -177,6 +177,13 @@ def _time_loop(torch, fn, sets, steps, warmup, batches=5):
     for i in range(warmup):
         fn(sets[i % len(sets)])
     torch.cuda.synchronize()
+    # then untimed calls until the row has run for at least 30 ms: the clocks
+    # take that long to settle after a change of load
+    t0, i = time.perf_counter(), warmup
+    while time.perf_counter() - t0 < 0.03:
+        fn(sets[i % len(sets)])
+        i += 1
+        torch.cuda.synchronize()
     nb = max(1, min(batches, steps))
     means, total, i0 = [], 0.0, 0
     for b in range(nb):
@@ -199,9 +206,10 @@ def copy_rate(torch):
 
 
 def bench_rows(nv, torch, wl, steps, warmup, copy_gbs):
-    """Every row gets ~10 ms or more of untimed warmup calls: the GPU's clocks
-    take milliseconds to settle after a change of load (the window attention
-    measured ~500 us right after the KV codec rows and ~430 us once settled)."""
+    """Every row gets its warmup calls and then at least 30 ms of further
+    untimed calls: the GPU's clocks take that long to settle after a change
+    of load (the window attention measured ~500 us right after the KV codec
+    rows and ~430 us once settled)."""
     out = {}
     stream = torch.cuda.current_stream()
 
