@@ -62,8 +62,8 @@ def _args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=200,
-                   help="untimed steps before the timed ones (200 steps, ~14 ms, let the GPU clocks settle)")
+    p.add_argument("--warmup", type=int, default=500,
+                   help="untimed steps before the timed ones (500 steps, ~30 ms, let the GPU clocks settle)")
     p.add_argument("--no-rows", action="store_true", help="skip the per-row extra measurements")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--sets", type=int, default=13, help="rotating buffer sets")
