@@ -241,3 +241,24 @@ def test_binding_refuses_host_tensors_and_mismatched_buffers(nv):
         wrong_dtype.c()
     with pytest.raises(ValueError, match="out must have shape"):
         nv.gemm(good, good, out=torch.zeros((3, 4)))
+
+
+def test_product_and_oracle_share_no_code():
+    """The product path (binding, HIP sources, header, bench's timed code path
+    through the binding) names nothing under oracle/, and the oracle names
+    nothing of the product; only workloads/ (seeded inputs) serves both."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    pkg = os.path.join(root, "nvfp4_w4a4_block_02_amd")
+    product = [os.path.join(pkg, "__init__.py"), os.path.join(pkg, "build.py"),
+               os.path.join(root, "include", "nvfp4.h")]
+    product += [os.path.join(pkg, "csrc", f) for f in os.listdir(os.path.join(pkg, "csrc"))]
+    for path in product:
+        text = open(path, encoding="utf-8").read()
+        assert not re.search(r"\boracle\b", text), path
+    for f in os.listdir(os.path.join(root, "oracle")):
+        if f.endswith(".py"):
+            text = open(os.path.join(root, "oracle", f), encoding="utf-8").read()
+            assert not re.search(r"^\s*(import|from)\s+nvfp4_w4a4_block_02_amd", text, re.M), f
+            assert "csrc" not in text and "libnvfp4" not in text, f
+    wl = open(os.path.join(root, "workloads", "__init__.py"), encoding="utf-8").read()
+    assert not re.search(r"^\s*(import|from)\s+(oracle|nvfp4_w4a4_block_02_amd)", wl, re.M)
