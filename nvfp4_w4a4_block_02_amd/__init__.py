@@ -397,10 +397,13 @@ def linear_train(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, sign_mask: 
     must give "dyt" / "xt" a K of M rounded up to 128."""
     b = bufs if bufs is not None else {}
     xq = quantize(x, axis=1, out=b.get("xq"), ws=b.get("ws"), stream=stream)
-    wq = quantize(w, axis=1, out=b.get("wq"), ws=b.get("ws"), stream=stream)
+    # W is quantized along both of its dims with one tensor scale: its amax
+    # does not depend on the block direction, so one amax pass serves both.
+    wamax = amax(w, out=b.get("wamax"), ws=b.get("ws"), stream=stream)
+    wq = encode(w, wamax, axis=1, out=b.get("wq"), stream=stream)
     y = gemm(xq, wq, out_dtype=torch.bfloat16, out=b.get("y"), stream=stream)
     dyq = quantize(dy, axis=1, out=b.get("dyq"), ws=b.get("ws"), stream=stream)
-    wtq = quantize(w, axis=0, out=b.get("wtq"), ws=b.get("ws"), stream=stream)
+    wtq = encode(w, wamax, axis=0, out=b.get("wtq"), stream=stream)
     dx = gemm(dyq, wtq, out_dtype=torch.bfloat16, out=b.get("dx"), stream=stream)
     # The weight gradient reduces over M; its operands are zero-padded to a
     # multiple of 128 along M (exact: zero blocks add nothing) so that the
