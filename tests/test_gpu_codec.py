@@ -50,6 +50,33 @@ def test_quantize_rows_matches_oracle(nv, rows, cols, dtype):
     assert_q_exact(gq, oracle.quantize(xh), f"{dtype} {rows}x{cols}")
 
 
+@pytest.mark.parametrize("rows,cols,ld", [(37, 96, 120), (300, 1040, 1056), (1, 16, 24)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantize_rows_strided_input(nv, rows, cols, ld, dtype):
+    """Axis 1 (blocks along the rows) from a view whose rows are ld > cols
+    elements apart: quantize, the RHT16 variant and the separate amax/encode
+    pair all read only the first cols of every row."""
+    log(f"quantize axis1 strided {dtype} {rows}x{cols} ld {ld}")
+    rng = np.random.default_rng(rows * 13 + ld)
+    xp = _rand(rng, rows, ld)
+    xp[:, cols:] = 1e30  # padding that would dominate any amax that read it
+    if dtype == "bf16":
+        bits = workloads.to_bf16_bits(xp)
+        xd, xh = dev_bf16(bits)[:, :cols], np.ascontiguousarray(widen(bits)[:, :cols])
+    else:
+        xd, xh = dev_f32(xp)[:, :cols], np.ascontiguousarray(xp[:, :cols])
+    assert rows == 1 or not xd.is_contiguous()
+    gq = nv.quantize(xd)
+    gr = nv.rht16_quantize(xd, 0x3C5A)
+    a = nv.amax(xd)
+    ge = nv.encode(xd, a)
+    torch.cuda.synchronize()
+    want = oracle.quantize(xh)
+    assert_q_exact(gq, want, f"strided {dtype}")
+    assert_q_exact(ge, want, f"strided amax+encode {dtype}")
+    assert_q_exact(gr, oracle.rht16_quantize(xh, 0x3C5A), f"strided rht {dtype}")
+
+
 @pytest.mark.parametrize("rows,cols", [(16, 16), (48, 33), (256, 130), (1040, 64)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_quantize_cols_matches_oracle(nv, rows, cols, dtype):
