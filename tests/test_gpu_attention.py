@@ -163,6 +163,23 @@ def test_extreme_query_rows_and_scales(nv):
     assert checked >= 4
 
 
+def test_all_zero_key_block(nv):
+    """A K frame block that is all zero (tensor scale 0): its keys score 0 for
+    every query, so they take part in the softmax with weight exp(-max)."""
+    frames, tokens, heads, q_frames, fb = 12, 32, 2, 3, 4
+    log("kv_attention all-zero K frame block")
+    rng = np.random.default_rng(79)
+    qbits, k, v = _case(rng, frames, tokens, heads, q_frames)
+    k[4:8] = 0.0
+    kq, vq = oracle.kv_quantize(k, fb), oracle.kv_quantize(v, fb)
+    assert kq.tscale[1] == 0.0
+    shape = (frames, tokens, heads, 128)
+    qf = widen(qbits).reshape(q_frames * tokens, heads, 128)
+    ref, scale = A.window_attention_ref(qf, kq, vq, frames, tokens, heads, 128, q_frames, fb)
+    bound = _score_bound(qf, kq, frames, tokens, heads, 128, q_frames, fb, np.arange(q_frames * tokens))
+    _check(_run(nv, qbits, kq, vq, shape, q_frames, fb, torch.float32), ref, scale, bound, False, "zero K block")
+
+
 def test_four_over_six_cache(nv):
     """The attention reads a cache written by the Four Over Six encoder
     unchanged (same format)."""

@@ -90,6 +90,21 @@ def test_tile_shapes_are_bit_identical(nv, m, n, k):
     assert np.any(outs[0] != cref.astype(np.float32))  # the float32 accumulation rounded somewhere
 
 
+def test_gemm_with_an_all_zero_operand(nv):
+    """A zero activation tensor quantizes to S = 0; the product is exactly 0
+    everywhere (no NaN from 0 * scale paths) and the output amax is 0."""
+    rng = np.random.default_rng(11)
+    b = (rng.standard_normal((300, 256)) * 0.02).astype(np.float32)
+    ga, gb = nv.quantize(dev_f32(np.zeros((200, 256), np.float32))), nv.quantize(dev_f32(b))
+    amax = torch.full((1,), 5.0, device="cuda")
+    for out_dtype in (torch.float32, torch.bfloat16):
+        c = nv.gemm(ga, gb, out_dtype=out_dtype, epilogue=nv.EPI_GELU_TANH, amax_out=amax)
+        torch.cuda.synchronize()
+        assert float(ga.tscale.cpu()[0]) == 0.0
+        assert torch.all(c.float().cpu() == 0.0)
+        assert amax.item() == 0.0
+
+
 def test_gemm_into_strided_output(nv):
     rng = np.random.default_rng(3)
     ga, gb, oa, ob = _operands(nv, rng, 70, 90, 256)
