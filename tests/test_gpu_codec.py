@@ -171,6 +171,26 @@ def test_amax_and_encode_with_given_amax(nv):
     assert np.array_equal(a3.cpu().numpy(), np.array(want, np.float32))
 
 
+def test_row_domains_encode_and_dequantize(nv):
+    """Row domains outside the KV layout: amax per 40-row group, encode with
+    those maxima (one tensor scale per group), decode with the same groups;
+    each group equals the oracle's quantization of that group on its own."""
+    rng = np.random.default_rng(12)
+    x = _rand(rng, 96, 160)
+    xd = dev_f32(x)
+    a3 = nv.amax(xd, rows_per_domain=40)
+    gq = nv.encode(xd, a3, rows_per_domain=40)
+    y = nv.dequantize(gq, torch.float32, rows_per_domain=40).cpu().numpy()
+    torch.cuda.synchronize()
+    codes, scales, ts = gq.codes.cpu().numpy(), gq.scales.cpu().numpy(), gq.tscale.cpu().numpy()
+    for d, (r0, r1) in enumerate([(0, 40), (40, 80), (80, 96)]):
+        oq = oracle.quantize(x[r0:r1])
+        assert np.array_equal(codes[r0:r1], oq.codes) and np.array_equal(scales[r0:r1], oq.scales), d
+        assert ts[d] == oq.tscale[0], d
+        want = oracle.dequantize(oq, "f32")
+        assert np.array_equal(y[r0:r1].view(np.uint32), want.view(np.uint32)), d
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_dequantize_matches_oracle(nv, dtype):
     rng = np.random.default_rng(8)
