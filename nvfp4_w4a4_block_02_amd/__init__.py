@@ -180,6 +180,7 @@ class NVFP4Tensor:
 
 
 def workspace_bytes(op: int, rows: int, cols: int) -> int:
+    """Device workspace bytes an entry point needs (nvfp4_workspace_bytes)."""
     return int(_lib().nvfp4_workspace_bytes(op, rows, cols))
 
 
@@ -206,6 +207,8 @@ def _out_shape(x: torch.Tensor, axis: int):
 
 def amax(x: torch.Tensor, rows_per_domain: int = 0, out: torch.Tensor | None = None,
          ws: torch.Tensor | None = None, stream=None):
+    """max |x| per domain of `rows_per_domain` rows (0: the whole tensor) into a
+    float32 tensor of one value per domain (nvfp4_amax)."""
     rows, cols = x.shape
     nd = 1 if rows_per_domain <= 0 or rows_per_domain >= rows else -(-rows // rows_per_domain)
     if out is None:
@@ -221,6 +224,8 @@ def amax(x: torch.Tensor, rows_per_domain: int = 0, out: torch.Tensor | None = N
 
 def encode(x: torch.Tensor, amax_t: torch.Tensor, axis: int = 1, rows_per_domain: int = 0,
            out: NVFP4Tensor | None = None, stream=None) -> NVFP4Tensor:
+    """Encode x with given per-domain maxima `amax_t` (nvfp4_encode): codes,
+    block scales and tscale = amax / 2688; axis 0 stores the transpose."""
     rows, cols = x.shape
     nd = 1 if rows_per_domain <= 0 or rows_per_domain >= rows else -(-rows // rows_per_domain)
     _need(amax_t, "amax", dtype=torch.float32, min_numel=nd)
@@ -310,6 +315,8 @@ def kv_quant(kv: torch.Tensor, frame_block: int = 8, out: NVFP4Tensor | None = N
 
 def kv_dequant(q: NVFP4Tensor, shape, frame_block: int = 8, out: torch.Tensor | None = None,
                stream=None) -> torch.Tensor:
+    """Decode an NVFP4 KV cache of `shape` = (frames, tokens, heads, head_dim)
+    to bf16 with its per-frame-block tensor scales (nvfp4_kv_dequant)."""
     f, t, h, d = shape
     if out is None:
         out = torch.empty((f, t, h, d), dtype=torch.bfloat16, device=q.codes.device)
@@ -343,6 +350,8 @@ def kv_attention(q: torch.Tensor, k: NVFP4Tensor, v: NVFP4Tensor, shape, frame_b
 
 def dequantize(q: NVFP4Tensor, dtype=torch.float32, rows_per_domain: int = 0, out: torch.Tensor | None = None,
                stream=None) -> torch.Tensor:
+    """Decode an NVFP4 tensor to float32 or bf16, one tensor scale per domain
+    of `rows_per_domain` rows (nvfp4_dequantize)."""
     if out is None:
         out = torch.empty((q.rows, q.k), dtype=dtype, device=q.codes.device)
     _need(out, "out", shape=(q.rows, q.k))
