@@ -240,6 +240,9 @@ def encode(x: torch.Tensor, amax_t: torch.Tensor, axis: int = 1, rows_per_domain
 
 def quantize(x: torch.Tensor, axis: int = 1, out: NVFP4Tensor | None = None, ws: torch.Tensor | None = None,
              stream=None) -> NVFP4Tensor:
+    """Quantize a float32/bf16 matrix to NVFP4 with one tensor scale
+    (nvfp4_quantize): blocks along the rows' elements (axis 1) or down the
+    columns (axis 0, output stored transposed)."""
     rows, cols = x.shape
     if out is None:
         r, k = _out_shape(x, axis)
