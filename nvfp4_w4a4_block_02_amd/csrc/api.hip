@@ -141,8 +141,11 @@ static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, i
   float* parts = static_cast<float*>(ws);
   hipError_t e;
   uint32_t np;
-  if (axis == 1 || !rht) {
-    // Without the transform the amax does not depend on the block direction.
+  if (axis == 1 || (!rht && cols % 16 == 0)) {
+    // Without the transform the amax does not depend on the block direction,
+    // and the row pass covers every column when they fill whole 16-element
+    // pieces.  Axis 0 accepts any column count: then the column pass, which
+    // handles the right edge, takes the amax.
     np = nvfp4::amax_parts_rows(rows, cols, 0);
     e = nvfp4::launch_amax_parts_rows(x, dtype, rows, cols, ld, 0, parts, np, rht, mask, s);
   } else {
@@ -254,12 +257,14 @@ int nvfp4_kv_attention(const void* q, int64_t q_frames, const nvfp4_tensor* k, c
   const int64_t nq = q_frames * tokens;  // <= rows
   if (nq == 0 || heads == 0) return NVFP4_OK;
   if (head_dim != 128) return NVFP4_EUNSUPPORTED;
-  const int64_t nfb = frames / frame_block + (frames % frame_block != 0);
-  if (nfb > 1 && (frame_block * tokens) % 64 != 0) return NVFP4_EUNSUPPORTED;  // frame_block < frames here
   if (((nq + 127) / 128) * heads >= ((int64_t)1 << 31)) return NVFP4_EUNSUPPORTED;
+  // One frame block covers the whole window when frame_block >= frames (as
+  // in nvfp4_kv_dequant); the kernel then sees at most frames * tokens keys
+  // per block.
+  const int64_t fb = frame_block < frames ? frame_block : frames;
   return from_hip(nvfp4::launch_kv_attention(static_cast<const uint16_t*>(q), qout(k), qout(v), out,
                                              out_dtype == NVFP4_F32, nq, tokens, heads, frames, q_frames,
-                                             frame_block, (hipStream_t)stream));
+                                             fb, (hipStream_t)stream));
 }
 
 int nvfp4_dequantize(const nvfp4_tensor* in, int64_t rows_per_domain, void* out, int dtype, void* stream) {

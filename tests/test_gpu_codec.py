@@ -97,6 +97,32 @@ def test_quantize_cols_matches_oracle(nv, rows, cols, dtype):
     assert_q_exact(gq, oracle.quantize(np.ascontiguousarray(xh.T)), f"axis0 {dtype} {rows}x{cols}")
 
 
+@pytest.mark.parametrize("rows,cols,ld,dtype", [(48, 8, 8, "bf16"), (32, 12, 12, "f32"), (64, 24, 24, "bf16"),
+                                                (256, 130, 136, "f32"), (48, 33, 40, "bf16"), (16, 4, 4, "f32")])
+def test_quantize_cols_amax_in_tail_column(nv, rows, cols, ld, dtype):
+    """Axis 0 takes any column count, so the tensor amax must cover the
+    columns past the last multiple of 16: the largest magnitude sits in the
+    last column (also with fewer than 16 columns, and with rows stored
+    contiguously, ld == cols)."""
+    log(f"quantize axis0 tail-column amax {dtype} {rows}x{cols} ld {ld}")
+    rng = np.random.default_rng(rows * 17 + cols)
+    x = _rand(rng, rows, cols, spread=1.0, outlier=0.0)
+    x[rows // 3, cols - 1] = -40.0 * np.abs(x).max()
+    xp = np.zeros((rows, ld), np.float32)
+    xp[:, :cols] = x
+    if dtype == "bf16":
+        bits = workloads.to_bf16_bits(xp)
+        xd, xh = dev_bf16(bits)[:, :cols], widen(bits)[:, :cols]
+    else:
+        xd, xh = dev_f32(xp)[:, :cols], xp[:, :cols]
+    assert (ld == cols) == xd.is_contiguous()
+    gq = nv.quantize(xd, axis=0)
+    torch.cuda.synchronize()
+    want = oracle.quantize(np.ascontiguousarray(xh.T))
+    assert want.tscale[0] == np.float32(np.abs(xh).max()) / np.float32(2688.0)
+    assert_q_exact(gq, want, f"axis0 tail {dtype} {rows}x{cols}")
+
+
 def test_hand_worked_blocks_on_gpu(nv, golden_dir):
     with open(os.path.join(golden_dir, "hand_blocks.json")) as f:
         cases = json.load(f)["cases"]
