@@ -261,11 +261,11 @@ int nvfp4_kv_dequant(const nvfp4_tensor *in, int64_t frames, int64_t tokens, int
  * an exact computation to about 2^-10 of sum_j p_j |V_j| / sum_j p_j per
  * element (plus the bf16 rounding of the output).
  *
- * Limits: head_dim must be 128 (else NVFP4_EUNSUPPORTED); 1 <= q_frames <=
- * frames; with more than one frame block, frame_block * tokens must be a
- * multiple of 64 (each 64-key tile lies in one frame block; else
- * NVFP4_EUNSUPPORTED).  A non-finite value anywhere in the keys a workgroup
- * of 128 queries scans can propagate to its outputs.  No workspace.
+ * Frame blocks may hold any number of keys (frame_block * tokens); a
+ * frame_block >= frames means one block over the whole window, as in
+ * nvfp4_kv_dequant.  Limits: head_dim must be 128 (else NVFP4_EUNSUPPORTED);
+ * 1 <= q_frames <= frames.  A non-finite value anywhere in the keys a
+ * workgroup of 128 queries scans can propagate to its outputs.  No workspace.
  */
 int nvfp4_kv_attention(const void *q, int64_t q_frames, const nvfp4_tensor *k, const nvfp4_tensor *v,
                        int64_t frames, int64_t tokens, int64_t heads, int64_t head_dim,

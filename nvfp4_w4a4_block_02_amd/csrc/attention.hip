@@ -44,6 +44,12 @@
 // scores of tile t+1 are computed while tile t's softmax runs, and tile t's
 // P V product overlaps the decode of the next tiles (raw codes loaded one
 // iteration earlier); one barrier per tile.
+//
+// Key tiles follow the frame blocks: the tiles of frame block b start at its
+// first key, so no tile mixes two tensor scales.  When a frame block is not a
+// whole number of tiles, its last tile is partial and its keys past the
+// block end are masked (they belong to the next block's first tile); when it
+// is (e.g. 8 frames of 880 tokens), tile t simply starts at key 64 t.
 #include <cmath>
 
 #include "device.h"
@@ -295,9 +301,16 @@ __device__ __forceinline__ void pv_tile(const uint8_t* vbuf, int c, int hf, cons
       }
 }
 
+// First key of key tile t with `tpb` tiles per frame block of fb_keys keys.
+__device__ __forceinline__ int tile_key0(int t, int tpb, int fb_keys) {
+  if (tpb * kKT == fb_keys) return t * kKT;   // blocks of whole tiles
+  const int b = t / tpb;
+  return b * fb_keys + (t - b * tpb) * kKT;
+}
+
 struct Ctx {
   uint8_t* smem;
-  int nt, c, hf, tid, lim, fb_keys;
+  int nt, c, hf, tid, lim, fb_keys, tpb;   // tpb: key tiles per frame block
   float cq;
   const float* kts;
   const float* vts;
@@ -314,7 +327,7 @@ __device__ __forceinline__ void step(const Ctx& x, int t, const half8_t (&qf)[8]
                                      float16_t (&scur)[2], State& st) {
   uint8_t* b0 = x.smem + (t & 1) * kBuf;        // K t+2 (write), V t (read)
   uint8_t* b1 = x.smem + ((t + 1) & 1) * kBuf;  // K t+1 (read), V t+1 (write)
-  const int key0 = t * kKT;
+  const int key0 = tile_key0(t, x.tpb, x.fb_keys);
   const int fb = key0 / x.fb_keys;
   // A new V tensor scale (once per frame block): re-express the accumulator
   // in it.  An all-zero V frame block (scale 0) decodes to zeros and keeps
@@ -329,7 +342,8 @@ __device__ __forceinline__ void step(const Ctx& x, int t, const half8_t (&qf)[8]
   float16_t snext[2];
   qk_tile(b1, x.c, x.hf, qf, snext);
   half8_t pb[2][2];
-  const float f = softmax_tile<MASK>(scur, key0, x.hf, x.cq, x.lim, x.kts[fb], st, pb);
+  // keys past the query's limit or past the frame block's end take no part
+  const float f = softmax_tile<MASK>(scur, key0, x.hf, x.cq, min(x.lim, (fb + 1) * x.fb_keys), x.kts[fb], st, pb);
   __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -353,8 +367,8 @@ __device__ __forceinline__ void step(const Ctx& x, int t, const half8_t (&qf)[8]
     __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (t + 3 < x.nt) load_raw_k(geo, (t + 3) * kKT, x.tid, raw);
-  if (t + 2 < x.nt) load_raw_v(geo, (t + 2) * kKT, x.tid, raw);
+  if (t + 3 < x.nt) load_raw_k(geo, tile_key0(t + 3, x.tpb, x.fb_keys), x.tid, raw);
+  if (t + 2 < x.nt) load_raw_v(geo, tile_key0(t + 2, x.tpb, x.fb_keys), x.tid, raw);
   __syncthreads();
   scur[0] = snext[0];
   scur[1] = snext[1];
@@ -384,7 +398,8 @@ __global__ __launch_bounds__(256, 2) void kv_attention_kernel(
   const int first_frame = frames - q_frames;
   const int qlast = min(q0 + kQT, nq) - 1;
   const int kmax = (first_frame + qlast / tokens + 1) * tokens;   // no query of the group sees keys >= kmax
-  const int nt = (kmax + kKT - 1) / kKT;
+  const int tpb = (fb_keys + kKT - 1) / kKT;                      // key tiles per frame block
+  const int nt = (kmax / fb_keys) * tpb + (kmax % fb_keys + kKT - 1) / kKT;
   // this wavefront's first query sees keys < kmin_w: tiles below need no mask
   const int qw = min(q0 + 32 * wave, nq - 1);
   const int kmin_w = (first_frame + qw / tokens + 1) * tokens;
@@ -447,11 +462,11 @@ __global__ __launch_bounds__(256, 2) void kv_attention_kernel(
   decode_k(raw, smem, tid);
   decode_v(raw, smem, tid);
   if (nt > 1) {
-    load_raw_k(geo, kKT, tid, raw);
+    load_raw_k(geo, tile_key0(1, tpb, fb_keys), tid, raw);
     decode_k(raw, smem + kBuf, tid);
   }
-  if (nt > 2) load_raw_k(geo, 2 * kKT, tid, raw);
-  if (nt > 1) load_raw_v(geo, kKT, tid, raw);
+  if (nt > 2) load_raw_k(geo, tile_key0(2, tpb, fb_keys), tid, raw);
+  if (nt > 1) load_raw_v(geo, tile_key0(1, tpb, fb_keys), tid, raw);
   __syncthreads();
   float16_t scur[2];
   qk_tile(smem, c, hf, qf, scur);
@@ -459,8 +474,12 @@ __global__ __launch_bounds__(256, 2) void kv_attention_kernel(
 
   // Tiles wholly below this wavefront's first query limit need no mask; the
   // two kinds run in two loops (one copy of the tile code each).
-  const Ctx cx{smem, nt, c, hf, tid, lim, fb_keys, cq, kts, vts};
-  const int nt_plain = min(kmin_w / kKT, nt);
+  const Ctx cx{smem, nt, c, hf, tid, lim, fb_keys, tpb, cq, kts, vts};
+  // Tiles wholly below the first query limit are unmasked; with partial
+  // block-end tiles only those before the first one (the first block's tiles
+  // start at 64 t, so "wholly below" is the same test there).
+  int nt_plain = min(kmin_w / kKT, nt);
+  if (tpb * kKT != fb_keys) nt_plain = min(nt_plain, tpb - 1);
   int t = 0;
   for (; t < nt_plain; ++t) step<false>(cx, t, qf, geo, raw, scur, st);
   for (; t < nt; ++t) step<true>(cx, t, qf, geo, raw, scur, st);
