@@ -6,6 +6,8 @@ format definition fixes, torch's own float8_e4m3fn and bfloat16 casts
 independently with ``fractions.Fraction``.
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from fractions import Fraction
 
 import numpy as np
@@ -112,16 +114,57 @@ def test_bf16_against_torch():
     assert np.array_equal(F.bf16_bits_to_f32(lib), torch.from_numpy(lib.view(np.int16)).view(torch.bfloat16).float().numpy())
 
 
-@pytest.mark.slow
-def test_e2m1_exhaustive_positive_range():
-    # Every float32 in [0, 8): the converter against the Fraction-free exact
-    # threshold rule, chunked.
+def _sweep(lo_bits: int, hi_bits: int, check, chunk: int = 1 << 24):
+    """Run check(float32 values) over every bit pattern in [lo_bits, hi_bits),
+    in chunks spread over a thread pool (NumPy releases the GIL in the
+    element-wise work).  Returns the number of patterns checked."""
+    starts = range(lo_bits, hi_bits, chunk)
+
+    def one(start):
+        b = np.arange(start, min(start + chunk, hi_bits), dtype=np.uint32)
+        check(b.view(np.float32))
+        return b.size
+
+    workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(workers) as ex:
+        return sum(ex.map(one, starts))
+
+
+def test_e2m1_exhaustive_nonnegative():
+    """Every non-negative float32 up to 8 (beyond the saturation point 5) and
+    every one of their negatives: the converter against the threshold rule
+    written from the grid (midpoints between neighbours, ties to the even
+    code), and sign symmetry (-y gives the code of y with bit 3 set).
+    Everything above 8 saturates like 8 does (sampled)."""
     thr = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
-    for start in range(0, 0x41000000, 1 << 26):
-        b = np.arange(start, min(start + (1 << 26), 0x41000000), dtype=np.uint32)
-        y = b.view(np.float32)
+
+    def check(y):
         got = F.f32_to_e2m1(y)
         yy = y.astype(np.float64)
-        # even-index ties: >= for thresholds whose upper neighbour is even
+        # ties (y == threshold) go up only where the upper neighbour is even
         want = sum(((yy >= t) if i % 2 == 1 else (yy > t)).astype(np.uint8) for i, t in enumerate(thr))
         assert np.array_equal(got, want)
+        assert np.array_equal(F.f32_to_e2m1(-y), want | 8)
+
+    n = _sweep(0, 0x41000001, check)
+    assert n == 0x41000001
+    big = np.random.default_rng(8).integers(0x41000000, 0x7F800000, 1 << 20, dtype=np.uint32).view(np.float32)
+    assert np.all(F.f32_to_e2m1(big) == 7) and np.all(F.f32_to_e2m1(-big) == 15)
+
+
+def test_e4m3_exhaustive_nonnegative():
+    """Every non-negative float32 below 464 (the midpoint between 448 and the
+    first unrepresentable 480, where saturation takes over): the converter
+    against torch's float8_e4m3fn cast (RNE; a library routine), and 448
+    (0x7E) from 464 up to the largest finite float32 (sampled, plus the
+    boundary patterns)."""
+    def check(y):
+        lib = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(F.f32_to_e4m3(y), lib)
+
+    n = _sweep(0, 0x43E80000, check)
+    assert n == 0x43E80000
+    hi = np.concatenate([np.arange(0x43E80000, 0x43E80000 + 4096, dtype=np.uint32),
+                         np.random.default_rng(9).integers(0x43E80000, 0x7F800000, 1 << 20, dtype=np.uint32),
+                         np.array([0x7F7FFFFF], np.uint32)]).view(np.float32)
+    assert np.all(F.f32_to_e4m3(hi) == 0x7E)

@@ -41,6 +41,32 @@ def test_hand_worked_blocks(golden_dir):
     assert np.array_equal(q2.codes, q.codes) and np.array_equal(q2.scales, q.scales)
 
 
+def test_error_sum_order_is_pinned(golden_dir):
+    """Block 5 of the golden is built so that the float32 error sums depend
+    on their order: summed from element 0 (the reading) the core candidate
+    is kept; summed from element 15 down, E4 < E6 and the choice would flip.
+    The expected errors are the hand-worked ones."""
+    g = _golden(golden_dir)
+    x = np.array(g["x"], np.float32)[None, 80:96]
+    assert g["keeps_four"][5] is False
+    s = np.float32(1.0)   # the golden's tensor scale (its first block holds 2688)
+    sig6, sig4 = fo6.block_scales_to(x, s, 6.0), fo6.block_scales_to(x, s, 4.0)
+    e6 = fo6.block_sq_error(x, oracle.encode(x, sig6, s), sig6, s)
+    e4 = fo6.block_sq_error(x, oracle.encode(x, sig4, s), sig4, s)
+    assert e6[0, 0] == np.float32(0.25) and e4[0, 0] == np.float32(0.25) + np.float32(2.0 ** -25)
+    # the same squared errors summed in the opposite order
+    d6 = np.array([0, 0.25, 2.0 ** -26, 2.0 ** -26, 0] + [0] * 11, np.float32)
+    d4 = np.array([0, 0, 2.0 ** -26, 2.0 ** -26, 0.25] + [0] * 11, np.float32)
+    rev = []
+    for d in (d6, d4):
+        e = np.float32(0)
+        for v in d[::-1]:
+            e = np.float32(e + v)
+        rev.append(e)
+    assert rev[1] < rev[0]          # reversed: mapping to 4 would win
+    assert not e4[0, 0] < e6[0, 0]  # the reading: the core scale is kept
+
+
 @pytest.fixture
 def rng():
     return np.random.default_rng(4060)

@@ -1,7 +1,11 @@
 """Pins for the oracle's 16-point random Hadamard transform (CPU only):
 the Sylvester matrix from two constructions, the butterfly on unit vectors
-(exact), orthogonality, the inverse, inner-product preservation and the
-float32 rounding bound against a float64 matrix product."""
+(exact), hand-worked float32 blocks that fix the butterfly stage order,
+orthogonality, the inverse, inner-product preservation and the float32
+rounding bound against a float64 matrix product."""
+
+import json
+import os
 
 import numpy as np
 
@@ -74,3 +78,29 @@ def test_rht_quantize_axis0_is_transposed_axis1():
     assert q0.codes.shape == (48, 32)
     assert np.array_equal(q0.codes, q1.codes) and np.array_equal(q0.scales, q1.scales)
     assert q0.tscale[0] == q1.tscale[0]
+
+
+def _butterflies(x, mask, order):
+    """A float32 RHT16 with the butterfly stages in `order` (the oracle's is
+    1, 2, 4, 8): only used to show that the golden blocks tell orders apart."""
+    w = (np.asarray(x, np.float32) * rht.sign_vector(mask)).astype(np.float32)
+    for h in order:
+        lo = np.array([i for i in range(16) if not i & h])
+        a, b = w[lo].copy(), w[lo + h].copy()
+        w[lo], w[lo + h] = a + b, a - b
+    return (w * np.float32(0.25)).astype(np.float32)
+
+
+def test_butterfly_stage_order_golden(golden_dir):
+    """Hand-worked blocks (tests/golden/rht16_butterfly_order.json) on which
+    the float32 result depends on the stage order: the oracle reproduces them
+    bit for bit, and the stage order 8, 4, 2, 1 does not."""
+    with open(os.path.join(golden_dir, "rht16_butterfly_order.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        x = np.array(c["x"], np.float32)[None, :]
+        want = np.array(c["out"], np.float32)
+        got = rht.rht16_rows(x, c["mask"])[0]
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), c["name"]
+        assert np.array_equal(_butterflies(x[0], c["mask"], (1, 2, 4, 8)), want)
+        assert not np.array_equal(_butterflies(x[0], c["mask"], (8, 4, 2, 1)), want), c["name"]
