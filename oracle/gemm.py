@@ -43,12 +43,20 @@ def gemm_ref(a: QTensor, b: QTensor, rows: slice | np.ndarray | None = None, wan
 
 
 def gelu_tanh(h) -> np.ndarray:
-    """GELU, tanh form: 0.5 h (1 + tanh(sqrt(2/pi) (h + 0.044715 h^3))), in
-    float64.  The pages do not name the FFN activation; this standard form is
-    the reading for the DiT FFN."""
+    """GELU, tanh form: g(h) = 0.5 h (1 + tanh(u)), u = sqrt(2/pi) (h +
+    0.044715 h^3), in float64.  The pages do not name the FFN activation; this
+    standard form is the reading for the DiT FFN.
+
+    Evaluated through the identity 0.5 (1 + tanh u) = 1 / (1 + e^(-2u)): the
+    same function, written so that the negative tail keeps its relative
+    precision.  Written as 1 + tanh(u), it cancels: below h of about -5.6
+    that sum is exactly 0 in float64, while g is about h e^(2u), a normal
+    number down to h of about -19."""
     h = np.asarray(h, dtype=np.float64)
     c = np.sqrt(2.0 / np.pi)
-    return 0.5 * h * (1.0 + np.tanh(c * (h + 0.044715 * h ** 3)))
+    u = c * (h + 0.044715 * h ** 3)
+    with np.errstate(over="ignore"):
+        return h / (1.0 + np.exp(-2.0 * u))
 
 
 def ffn_chain(x: np.ndarray, w1: QTensor, w2: QTensor):

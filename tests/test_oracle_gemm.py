@@ -5,6 +5,8 @@ against torch's tanh-approximate GELU (a library routine)."""
 
 from fractions import Fraction
 
+from decimal import Decimal, localcontext
+
 import numpy as np
 import torch
 
@@ -80,13 +82,48 @@ def test_single_block_and_orientation():
 
 
 def test_gelu_against_torch():
-    h = np.concatenate([np.linspace(-12, 12, 2001), [0.0, 1.0, -1.0, 1e-8, 40.0]])
+    """torch's gelu(approximate="tanh") (a library routine) where its own
+    1 + tanh(u) does not cancel (h >= -2; below that torch loses relative
+    precision, about 3e-10 at h = -5, and the decimal pin takes over)."""
+    h = np.concatenate([np.linspace(-2, 12, 1401), [0.0, 1.0, -1.0, 1e-8, 40.0]])
     ours = oracle.gelu_tanh(h)
     lib = torch.nn.functional.gelu(torch.from_numpy(h), approximate="tanh").numpy()
-    assert np.allclose(ours, lib, rtol=1e-13, atol=1e-14)  # cancellation in the far negative tail
+    assert np.allclose(ours, lib, rtol=1e-13, atol=1e-300)
     assert oracle.gelu_tanh(0.0) == 0.0
     # the tanh part is odd: g(h) - g(-h) = h
     assert np.allclose(oracle.gelu_tanh(h) - oracle.gelu_tanh(-h), h, rtol=1e-12, atol=1e-12)
+
+
+_PI = "3.14159265358979323846264338327950288419716939937510582097494459230781640628620899862803482534211706798"
+
+
+def _gelu_decimal(h: float) -> float:
+    """The definition 0.5 h (1 + tanh(u)), tanh(u) = (e^(2u) - 1) / (e^(2u) + 1),
+    in 420-digit decimal arithmetic from the exact float64 input: enough
+    digits that 1 + tanh(u) keeps its value down to e^(2u) ~ 1e-310."""
+    with localcontext() as ctx:
+        ctx.prec = 420
+        x = Decimal(h)
+        c = (Decimal(2) / Decimal(_PI)).sqrt()
+        u = c * (x + Decimal("0.044715") * x ** 3)
+        e = (2 * u).exp()
+        t = (e - 1) / (e + 1)
+        return float(Decimal("0.5") * x * (1 + t))
+
+
+def test_gelu_against_high_precision_definition():
+    """Every float64 result, the far negative tail included, within the
+    rounding of its float64 evaluation of the definition computed to 420
+    digits: the exponent argument 2u carries a relative error of a few
+    2^-53, which moves e^(-2u) by |2u| times that."""
+    rng = np.random.default_rng(15)
+    h = np.concatenate([np.linspace(-19, 20, 391), rng.uniform(-19, 20, 200), [-1e-3, 1e-3, -0.5, 2.5]])
+    ours = oracle.gelu_tanh(h)
+    ref = np.array([_gelu_decimal(float(v)) for v in h])
+    u = np.sqrt(2 / np.pi) * (h + 0.044715 * h ** 3)
+    assert np.all(ours[h < -6] != 0.0) and np.all(ref[h < -6] != 0.0)   # the tail is not flushed
+    rtol = 2.0 ** -52 * (8 + 4 * np.abs(u))
+    assert np.all(np.abs(ours - ref) <= rtol * np.abs(ref) + 1e-320)
 
 
 def test_ffn_chain_wiring():
