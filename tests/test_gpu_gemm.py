@@ -5,7 +5,9 @@ quantization, so both sides multiply the same NVFP4 numbers.  Covers ragged
 M/N/K tails (the K-checked path and the K % 128 fast path), fp32/bf16
 outputs, the GELU epilogue with its amax reduction, and the workload shapes
 (tiny linear, attention projection, FFN pair stage by stage, weight-gradient
-GEMM after the RHT) at full size."""
+GEMM after the RHT, the training triple) at full size, where every output row
+is compared (the float64 bound is computed in row chunks to cap host
+memory)."""
 
 import numpy as np
 import pytest
@@ -158,6 +160,22 @@ def test_gelu_epilogue_and_amax(nv, m, n, k):
 
 
 # ---------------------------------------------------------------- workloads
+def _all_rows_close(gpu, oa, ob, out_bf16, tag, chunk=2048, keep=False):
+    """Every row of a GPU GEMM result against gemm_ref, the float64 result
+    and its bound computed `chunk` rows at a time.  Returns the largest
+    err / bound and, with ``keep``, the float64 oracle result."""
+    m = gpu.shape[0]
+    worst, parts = 0.0, []
+    for r0 in range(0, m, chunk):
+        rows = slice(r0, min(m, r0 + chunk))
+        cref, bound = oracle.gemm_ref(oa, ob, rows=rows)
+        worst = max(worst, assert_gemm_close(gpu[rows], cref, bound, out_bf16, f"{tag} rows {r0}+"))
+        if keep:
+            parts.append(cref)
+    log(f"  {tag}: all {m} rows within bound, max err/bound {worst:.3e}")
+    return worst, (np.concatenate(parts) if keep else None)
+
+
 def test_tiny_linear_full(nv):
     d = workloads.tiny_linear()
     log("workload 1: 256x512 @ 512x512 -> f32")
@@ -175,14 +193,70 @@ def test_attn_proj_full(nv):
     d = workloads.attn_proj()
     log("workload 2: X bf16 2640x3072 (act-quant) @ W 3072x3072 -> bf16")
     gw = nv.quantize(dev_f32(d["w"]))
-    y = nv.linear(dev_bf16(d["x"]), gw)
+    xq = nv.NVFP4Tensor.empty(2640, 3072, 1, "cuda")
+    y = nv.linear(dev_bf16(d["x"]), gw, xq=xq)
     ox, ow = oracle.quantize(widen(d["x"])), oracle.quantize(d["w"])
-    cref, bound = oracle.gemm_ref(ox, ow)
-    assert_gemm_close(y.float().cpu().numpy(), cref, bound, True, "workload 2")
+    torch.cuda.synchronize()
+    assert_q_exact(xq, ox, "X (the linear layer's own activation operand)")
+    assert_q_exact(gw, ow, "W")
+    _all_rows_close(y.float().cpu().numpy(), ox, ow, True, "workload 2")
+
+
+def _gelu_check(h, pre, tag):
+    """Stage (ii) of the FFN chain: the GELU-tanh epilogue (float32 H of the
+    fused GEMM1) against the float64 GELU of the GPU's own float32 GEMM1
+    output `pre` (same accumulation, same tensor scales; no epilogue), all
+    elements, in row chunks.
+
+    Tolerance in float32 ulps of the result: 4, plus the conditioning of the
+    float32 exponent argument.  The kernel evaluates
+    g = h / (1 + 2^w), w = -2 sqrt(2/pi) log2(e) (h + 0.044715 h^3), in
+    float32: w carries a relative rounding error of a few 2^-24 (constants,
+    cube, sum, product), which moves 2^w by ln2 |w| times that and g by the
+    share e/(1+e) of it (e = 2^w).  For h > 0 (e small) this vanishes; in the
+    negative tail, where g ~ h 2^-w underflows towards 0, it grows with |w|
+    for any float32 evaluation of the argument.  So the bound is
+    (4 + 5 |w| e/(1+e)) ulp(g), plus |h| 2^-126: where 1 + e exceeds 2^126
+    the hardware reciprocal flushes its would-be-subnormal result, so the
+    epilogue returns -0 for |g| < |h| 2^-126 (err/tol then approaches 1 at
+    that boundary, by construction).  Observed: at most ~2.5 ulp where the
+    argument's conditioning is negligible."""
+    kw = -2.0 * np.sqrt(2.0 / np.pi) * np.log2(np.e)
+    worst_flat, worst = 0.0, 0.0
+    for r0 in range(0, h.shape[0], 1024):
+        hh = h[r0:r0 + 1024].astype(np.float64)
+        x = pre[r0:r0 + 1024].astype(np.float64)
+        g = oracle.gelu_tanh(x)
+        w = kw * (x + 0.044715 * x ** 3)
+        with np.errstate(over="ignore"):
+            share = 1.0 / (1.0 + np.exp2(-w))   # e / (1 + e), e = 2^w
+        ulp = np.spacing(np.abs(g).astype(np.float32)).astype(np.float64)
+        err = np.abs(hh - g) / ulp
+        tol = 4.0 + 5.0 * np.abs(w) * share + np.abs(x) * 2.0 ** -126 / ulp
+        bad = np.argwhere(err > tol)
+        if bad.size:
+            i = tuple(bad[0])
+            raise AssertionError(f"{tag}: {len(bad)} GELU outputs outside tolerance; first row {r0 + i[0]}: "
+                                 f"pre {x[i]!r} gpu {hh[i]!r} ref {g[i]!r} err {err[i]:.2f} ulp tol {tol[i]:.2f}")
+        flat = np.abs(w) * share < 0.05      # well-conditioned part
+        if flat.any():
+            worst_flat = max(worst_flat, float(err[flat].max()))
+        worst = max(worst, float((err / tol).max()))
+    log(f"  {tag}: max GELU error {worst_flat:.2f} ulp where well conditioned; max err/tol {worst:.3f}")
 
 
 def _ffn_stagewise(nv, m, dmodel, f, seed):
-    """FFN pair stage by stage; every expected value is the oracle's own."""
+    """FFN pair stage by stage, every output compared; every expected value
+    is the oracle's own, fed the GPU's intermediate where the stage says so:
+    (i) GEMM1 (float32) within the GEMM bound; (ii) the GELU epilogue against
+    float64 GELU of the GPU's GEMM1 output, and its amax equal to max|H|;
+    (iii) the re-quantization of the GPU's own H with the epilogue's amax,
+    bit-exact against the oracle quantizer fed that H and amax; (iv) GEMM2
+    on those codes within the GEMM bound; (v) the fused ffn() equal to the
+    staged result bit for bit, and its distance to the full-oracle chain
+    reported (rounding-boundary code flips are expected there).
+    (i) and (ii) together bound |H - gelu(C1_oracle)| by the stage-(ii)
+    tolerance plus 1.13 (max |gelu'|) times the GEMM bound."""
     d = workloads.ffn(m=m, d=dmodel, f=f, seed=seed)
     xd = dev_bf16(d["x"])
     gw1, gw2 = nv.quantize(dev_f32(d["w1"])), nv.quantize(dev_f32(d["w2"]))
@@ -193,41 +267,37 @@ def _ffn_stagewise(nv, m, dmodel, f, seed):
     assert_q_exact(gx, ox, "X")
     assert_q_exact(gw1, ow1, "W1")
     assert_q_exact(gw2, ow2, "W2")
-    rows = np.unique(np.concatenate([[0, m - 1], np.random.default_rng(seed).integers(0, m, 48)]))
-    c1, _ = oracle.gemm_ref(ox, ow1, want_bound=False)     # all rows: H needs them
-    _, b1 = oracle.gemm_ref(ox, ow1, rows=rows)
-    # (i) GEMM1 alone, float32 out
-    g1 = nv.gemm(gx, gw1, out_dtype=torch.float32)
-    assert_gemm_close(g1.cpu().numpy()[rows], c1[rows], b1, False, "GEMM1")
-    del g1
+    # (i) GEMM1 alone, float32 out, every row
+    g1 = nv.gemm(gx, gw1, out_dtype=torch.float32).cpu().numpy()
+    _, c1 = _all_rows_close(g1, ox, ow1, False, "GEMM1", keep=True)
     # (ii) GEMM1 with the GELU epilogue and its amax
     hmax = torch.empty(1, device="cuda")
     h = nv.gemm(gx, gw1, out_dtype=torch.float32, epilogue=nv.EPI_GELU_TANH, amax_out=hmax)
-    g = oracle.gelu_tanh(c1[rows])
     hh = h.cpu().numpy()
-    tol = 1.13 * 1e-5 * b1 + 8 * np.spacing(np.abs(g).astype(np.float32)).astype(np.float64) + 1e-37
-    assert np.all(np.abs(hh[rows] - g) <= tol)
-    assert hmax.item() == float(np.abs(hh).max())
-    # (iii) re-quantization of H: the GPU encoder on the oracle's float32 H
-    # must reproduce the oracle's codes exactly
-    h32 = oracle.gelu_tanh(c1).astype(np.float32)
-    oh = oracle.quantize(h32)
-    gh = nv.quantize(dev_f32(h32))
+    _gelu_check(hh, g1, "GELU epilogue")
+    del g1
+    hm = np.float32(hmax.item())
+    assert hm == oracle.amax(hh)
+    # (iii) re-quantization of the GPU's own H with the epilogue's amax
+    gh = nv.encode(h, hmax)
+    oh = oracle.quantize_with_amax(hh, hm)
     torch.cuda.synchronize()
-    assert_q_exact(gh, oh, "H requant")
-    # (iv) GEMM2 on the oracle's H codes
-    c2, b2 = oracle.gemm_ref(oh, ow2, rows=rows)
+    assert_q_exact(gh, oh, "H requant (GPU H, GPU amax)")
+    # (iv) GEMM2 on those codes, every row
     y2 = nv.gemm(gh, gw2, out_dtype=torch.bfloat16)
-    assert_gemm_close(y2.float().cpu().numpy()[rows], c2, b2, True, "GEMM2")
-    # (v) the fused GPU chain against the full-oracle chain (reported; code
-    # flips at rounding boundaries are expected, so only a loose bound)
-    y = nv.ffn(xd, gw1, gw2).float().cpu().numpy()
-    rel = np.linalg.norm(y[rows] - c2) / np.linalg.norm(c2)
-    log(f"FFN chain relative Frobenius error vs full oracle: {rel:.3e}")
+    y2h = y2.float().cpu().numpy()
+    _all_rows_close(y2h, oh, ow2, True, "GEMM2")
+    del oh, hh
+    # (v) the fused chain is the staged chain; distance to the full oracle
+    y = nv.ffn(xd, gw1, gw2)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "fused ffn() differs from its stages"
+    rows = np.unique(np.concatenate([[0, m - 1], np.random.default_rng(seed).integers(0, m, 48)]))
+    oh_chain = oracle.quantize(oracle.gelu_tanh(c1).astype(np.float32))
+    c2, _ = oracle.gemm_ref(oh_chain, ow2, rows=rows, want_bound=False)
+    rel = np.linalg.norm(y2h[rows] - c2) / np.linalg.norm(c2)
+    log(f"  FFN chain relative Frobenius error vs full oracle chain: {rel:.3e}")
     assert rel < 1e-2
-    # the GPU amax drives the same tensor scale the oracle derives from its H
-    ts_gpu = np.float32(hmax.item()) / np.float32(2688.0)
-    assert abs(float(ts_gpu) - float(oh.tscale[0])) <= 1e-5 * float(oh.tscale[0])
 
 
 def test_ffn_pair_reduced(nv):
@@ -253,40 +323,44 @@ def test_wgrad_after_rht_full(nv):
     assert_q_exact(gg, og, "G")
     assert_q_exact(gx, ox, "X")
     c = nv.gemm(gg, gx, out_dtype=torch.float32).cpu().numpy()
-    rows = np.unique(np.concatenate([[0, 3071], np.random.default_rng(5).integers(0, 3072, 64)]))
-    cref, bound = oracle.gemm_ref(og, ox, rows=rows)
-    assert_gemm_close(c[rows], cref, bound, False, "workload 5")
+    _all_rows_close(c, og, ox, False, "workload 5", chunk=1024)
+
+
+def _padded_equal(gq, want, k_pad, tag):
+    """An axis-0 operand zero-padded along K to k_pad: the oracle's bytes,
+    then zero codes and zero scales."""
+    codes, scales = gq.codes.cpu().numpy(), gq.scales.cpu().numpy()
+    kc, ks = want.codes.shape[1], want.scales.shape[1]
+    assert codes.shape == (want.codes.shape[0], k_pad // 2), tag
+    assert np.array_equal(codes[:, :kc], want.codes) and not codes[:, kc:].any(), tag
+    assert np.array_equal(scales[:, :ks], want.scales) and not scales[:, ks:].any(), tag
+    assert gq.tscale.cpu().numpy()[0] == want.tscale[0], tag
 
 
 @pytest.mark.timeout(600)
 def test_train_linear_triple_full(nv):
     """Workload 6 (the training slice of the attention projection): forward,
-    input gradient and weight gradient, every operand bit-exact against the
-    oracle's quantizers and every GEMM within the parity bound on sampled rows."""
+    input gradient and weight gradient.  The six operands linear_train
+    itself built (passed in as buffers) are compared with the oracle's
+    quantizers byte for byte (the two RHT16 operands with their zero padding
+    from M = 2640 to 2688), and every row of the three GEMMs is within the
+    parity bound."""
     d = workloads.train_linear()
     log("workload 6: training triple of a 2640x3072x3072 linear layer")
     x, w, dy = dev_bf16(d["x"]), dev_f32(d["w"]), dev_bf16(d["dy"])
-    y, dx, dw = nv.linear_train(x, w, dy, d["mask"])
+    m, k, n, mp = 2640, 3072, 3072, 2688
+    bufs = {"xq": nv.NVFP4Tensor.empty(m, k), "wq": nv.NVFP4Tensor.empty(n, k), "dyq": nv.NVFP4Tensor.empty(m, n),
+            "wtq": nv.NVFP4Tensor.empty(k, n), "dyt": nv.NVFP4Tensor.empty(n, mp), "xt": nv.NVFP4Tensor.empty(k, mp)}
+    y, dx, dw = nv.linear_train(x, w, dy, d["mask"], bufs=bufs)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(6)
-    rows = {"m": np.unique(np.concatenate([[0, 2639], rng.integers(0, 2640, 40)])),
-            "n": np.unique(np.concatenate([[0, 3071], rng.integers(0, 3072, 40)]))}
-    r = oracle.linear_train_ref(widen(d["x"]), d["w"], widen(d["dy"]), d["mask"], rows=rows)
-    # the quantized operands, recomputed through the same entry points
-    assert_q_exact(nv.quantize(x), r["xq"], "X")
-    assert_q_exact(nv.quantize(w), r["wq"], "W")
-    assert_q_exact(nv.quantize(dy), r["dyq"], "dY")
-    assert_q_exact(nv.quantize(w, axis=0), r["wtq"], "W along dim 0")
-    assert_q_exact(nv.rht16_quantize(dy, d["mask"], axis=0), r["dyt"], "RHT dY along dim 0")
-    assert_q_exact(nv.rht16_quantize(x, d["mask"], axis=0), r["xt"], "RHT X along dim 0")
-    # the padded operands linear_train feeds the weight-gradient GEMM (M = 2640
-    # padded to 2688): the oracle's bytes, then zero codes and zero scales
-    for src, want, tag in ((dy, r["dyt"], "dY"), (x, r["xt"], "X")):
-        gp = nv.rht16_quantize(src, d["mask"], axis=0, k_pad=2688)
-        codes, scales = gp.codes.cpu().numpy(), gp.scales.cpu().numpy()
-        assert np.array_equal(codes[:, :1320], want.codes) and not codes[:, 1320:].any(), tag
-        assert np.array_equal(scales[:, :165], want.scales) and not scales[:, 165:].any(), tag
-        assert gp.tscale.cpu().numpy()[0] == want.tscale[0], tag
-    assert_gemm_close(y.float().cpu().numpy()[rows["m"]], r["y"], r["by"], True, "forward")
-    assert_gemm_close(dx.float().cpu().numpy()[rows["m"]], r["dx"], r["bdx"], True, "input gradient")
-    assert_gemm_close(dw.cpu().numpy()[rows["n"]], r["dw"], r["bdw"], False, "weight gradient")
+    r = oracle.linear_train_ref(widen(d["x"]), d["w"], widen(d["dy"]), d["mask"])
+    assert_q_exact(bufs["xq"], r["xq"], "X")
+    assert_q_exact(bufs["wq"], r["wq"], "W")
+    assert_q_exact(bufs["dyq"], r["dyq"], "dY")
+    assert_q_exact(bufs["wtq"], r["wtq"], "W along dim 0")
+    _padded_equal(bufs["dyt"], r["dyt"], mp, "RHT dY along dim 0, padded")
+    _padded_equal(bufs["xt"], r["xt"], mp, "RHT X along dim 0, padded")
+    for gpu, c, b, bf, tag in ((y, r["y"], r["by"], True, "forward"), (dx, r["dx"], r["bdx"], True, "input gradient"),
+                               (dw, r["dw"], r["bdw"], False, "weight gradient")):
+        worst = assert_gemm_close(gpu.float().cpu().numpy(), c, b, bf, tag)
+        log(f"  {tag}: all rows within bound, max err/bound {worst:.3e}")
