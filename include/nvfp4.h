@@ -29,9 +29,10 @@
  *
  * Conventions shared by every entry point:
  *   - Ownership: the caller owns every buffer (inputs, outputs, workspace).
- *     The library never allocates or frees memory and keeps no mutable global
- *     state, so concurrent calls on different streams are safe as long as
- *     their buffers do not overlap.
+ *     The library never allocates or frees memory.  Apart from the 4 KiB
+ *     per-GPU scratch array of nvfp4_quantize_noalloc it keeps no mutable
+ *     global state, so concurrent calls on different streams are safe as
+ *     long as their buffers do not overlap.
  *   - Pointers named x / c / out / codes / scales / tscale / amax / ws are
  *     DEVICE pointers; the nvfp4_tensor structs themselves live in HOST memory
  *     and are read before the call returns.
@@ -148,6 +149,25 @@ int nvfp4_encode(const void *x, int dtype, int64_t rows, int64_t cols, int64_t l
 int nvfp4_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                    int axis, const nvfp4_tensor *out, void *ws, size_t ws_bytes,
                    void *stream);
+
+/*
+ * nvfp4_quantize without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The amax pass's partial maxima go to a
+ * 4 KiB device array inside the library instead, one per GPU, held until the
+ * process ends; its device address is looked up once per device, on the
+ * first call for the device that runs `stream`, and no call allocates.
+ * Every call on a GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (on different streams) race, and the caller must serialize them.
+ * Nothing in the array needs clearing (each call writes every partial it
+ * reads).  The array holds the partial maxima of every tensor
+ * nvfp4_quantize accepts (at most 1024 floats), so no valid size is refused
+ * for lack of room (that check returns NVFP4_EWORKSPACE); NVFP4_EHIP if the
+ * array's address cannot be obtained.  Arguments, results and the other
+ * errors as nvfp4_quantize.
+ */
+int nvfp4_quantize_noalloc(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                           int axis, const nvfp4_tensor *out, void *stream);
 
 /*
  * Random Hadamard transform then quantize (gradient path: the pages apply an

@@ -56,6 +56,7 @@ def _load():
         "nvfp4_amax": (I, [P, I, I64, I64, I64, I64, P, P, SZ, P]),
         "nvfp4_encode": (I, [P, I, I64, I64, I64, I, I64, P, TP, P]),
         "nvfp4_quantize": (I, [P, I, I64, I64, I64, I, TP, P, SZ, P]),
+        "nvfp4_quantize_noalloc": (I, [P, I, I64, I64, I64, I, TP, P]),
         "rht16_quantize": (I, [P, I, I64, I64, I64, I, U32, TP, P, SZ, P]),
         "nvfp4_gemm": (I, [TP, TP, P, I, I64, I, P, P, SZ, P]),
         "nvfp4_gemm_tiled": (I, [TP, TP, P, I, I64, I, P, I, I, P]),
@@ -89,7 +90,7 @@ def __getattr__(name):  # module attribute `lib` loads the library on first acce
 
 
 EXPORTED = ("nvfp4_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_amax",
-            "nvfp4_encode", "nvfp4_quantize", "rht16_quantize", "nvfp4_gemm", "nvfp4_gemm_tiled", "nvfp4_kv_quant",
+            "nvfp4_encode", "nvfp4_quantize", "nvfp4_quantize_noalloc", "rht16_quantize", "nvfp4_gemm", "nvfp4_gemm_tiled", "nvfp4_kv_quant",
             "nvfp4_kv_quant_4over6", "nvfp4_kv_dequant", "nvfp4_dequantize", "nvfp4_kv_attention")
 
 
@@ -253,6 +254,21 @@ def quantize(x: torch.Tensor, axis: int = 1, out: NVFP4Tensor | None = None, ws:
     ct = out.c()
     _check(_lib().nvfp4_quantize(_ptr(x), _dtype_code(x), rows, cols, _ld(x), axis, ctypes.byref(ct),
                               _ptr(ws), ws.numel() * 4, _stream(stream)), "nvfp4_quantize")
+    return out
+
+
+def quantize_noalloc(x: torch.Tensor, axis: int = 1, out: NVFP4Tensor | None = None, stream=None) -> NVFP4Tensor:
+    """nvfp4_quantize without a workspace (nvfp4_quantize_noalloc): the
+    library keeps the partial maxima in its own per-GPU scratch array, so the
+    call allocates nothing when ``out`` is given.  Calls that overlap in time
+    on one GPU race on that array."""
+    rows, cols = x.shape
+    if out is None:
+        r, k = _out_shape(x, axis)
+        out = NVFP4Tensor.empty(r, k, 1, x.device)
+    ct = out.c()
+    _check(_lib().nvfp4_quantize_noalloc(_ptr(x), _dtype_code(x), rows, cols, _ld(x), axis, ctypes.byref(ct),
+                                         _stream(stream)), "nvfp4_quantize_noalloc")
     return out
 
 

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "internal.h"
 
 namespace {
@@ -59,6 +61,42 @@ int check_dense_to_q(const void* x, int dt, int64_t rows, int64_t cols, int64_t 
       mul_sat(out->k / 16 + 1, out->rows + 1) > kMaxBlocks)
     return NVFP4_EUNSUPPORTED;
   return NVFP4_OK;
+}
+
+// Scratch of nvfp4_quantize_noalloc: the amax pass's partial maxima of its
+// one scaling domain (at most kMaxParts floats), in a device array that each
+// GPU holds until the process ends, so that the call allocates nothing.  The
+// array's host-side name is not a device address: kernels get the address
+// hipGetSymbolAddress returns for the device, looked up once per device and
+// cached here.
+constexpr size_t kScratchFloats = nvfp4::kMaxParts;  // 4 KiB
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+constexpr int kMaxDevices = 256;
+std::atomic<float*> g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the NULL stream); nullptr if HIP cannot provide it.  The first
+// call for a device looks the address up with that device current.
+float* scratch_on(hipStream_t stream) {
+  int dev = -1;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  void* addr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (e != hipSuccess || addr == nullptr) return nullptr;
+  g_scratch[dev].store(static_cast<float*>(addr), std::memory_order_release);
+  return static_cast<float*>(addr);
 }
 
 }  // namespace
@@ -166,6 +204,17 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t
 int rht16_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int axis,
                    uint32_t sign_mask, const nvfp4_tensor* out, void* ws, size_t ws_bytes, void* stream) {
   return quantize_impl(x, dtype, rows, cols, ld, axis, true, sign_mask, out, ws, ws_bytes, stream);
+}
+
+int nvfp4_quantize_noalloc(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int axis,
+                           const nvfp4_tensor* out, void* stream) {
+  int st = check_dense_to_q(x, dtype, rows, cols, ld, axis, out);
+  if (st != NVFP4_OK) return st;
+  if (nvfp4_workspace_bytes(NVFP4_OP_QUANTIZE, rows, cols) > sizeof(scratch)) return NVFP4_EWORKSPACE;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  float* ws = scratch_on(static_cast<hipStream_t>(stream));
+  if (ws == nullptr) return NVFP4_EHIP;
+  return quantize_impl(x, dtype, rows, cols, ld, axis, false, 0, out, ws, sizeof(scratch), stream);
 }
 
 static int gemm_impl(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int c_dtype, int64_t ldc,

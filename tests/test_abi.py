@@ -101,6 +101,24 @@ def test_quantize_rejects_bad_arguments(nv):
     assert q(ctypes.c_void_p(FAKE), 1, 4, 0, 0, 1, ctypes.byref(_t(nv, 4, 0)), ws, 4096, _stream()) == 0
 
 
+def test_quantize_noalloc_rejects_bad_arguments(nv):
+    """The no-workspace quantizer checks its arguments like nvfp4_quantize,
+    on the host, before it touches HIP (no device needed here)."""
+    q = nv.lib.nvfp4_quantize_noalloc
+    good = _t(nv, 4, 32)
+    EINVAL = -1
+    assert q(None, 1, 4, 32, 32, 1, ctypes.byref(good), _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 7, 4, 32, 32, 1, ctypes.byref(good), _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE + 2), 1, 4, 32, 32, 1, ctypes.byref(good), _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 2, ctypes.byref(good), _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 1, ctypes.byref(_t(nv, 5, 32)), _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 20, 32, 32, 0, ctypes.byref(_t(nv, 32, 20)), _stream()) == EINVAL
+    assert q(ctypes.c_void_p(FAKE), 1, 1 << 40, 1 << 40, 1 << 40, 1, ctypes.byref(_t(nv, 1 << 40, 1 << 40)),
+             _stream()) == -2
+    # zero-sized problems are a no-op
+    assert q(ctypes.c_void_p(FAKE), 1, 0, 32, 32, 1, ctypes.byref(_t(nv, 0, 32)), _stream()) == 0
+
+
 def test_rht_rejects_wide_mask(nv):
     good = _t(nv, 4, 32)
     st = nv.lib.rht16_quantize(ctypes.c_void_p(FAKE), 1, 4, 32, 32, 1, 1 << 16, ctypes.byref(good),
