@@ -146,10 +146,10 @@ int nvfp4_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
   const int64_t nd = ndomains(rows, rows_per_domain);
   if (cols == 0) return from_hip(nvfp4::launch_zero(amax, nd, s));
   float* parts = static_cast<float*>(ws);
-  const uint32_t np = nvfp4::amax_parts_rows(rows, cols, rows_per_domain);
-  if (nvfp4::launch_amax_parts_rows(x, dtype, rows, cols, ld, rows_per_domain, parts, np, false, 0, s) != hipSuccess)
+  const nvfp4::DomGrid pg = nvfp4::amax_grid_rows(rows, cols, rows_per_domain);  // pg.ndom == nd
+  if (nvfp4::launch_amax_parts_rows(x, dtype, rows, cols, ld, rows_per_domain, parts, pg, false, 0, s) != hipSuccess)
     return NVFP4_EHIP;
-  return from_hip(nvfp4::launch_reduce_parts(parts, np, nd, amax, s));
+  return from_hip(nvfp4::launch_reduce_parts(parts, pg, amax, s));
 }
 
 int nvfp4_encode(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int axis,
@@ -160,10 +160,12 @@ int nvfp4_encode(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
   if (axis == 0 && rows_per_domain != 0) return NVFP4_EINVAL;
   if (rows == 0 || cols == 0) return NVFP4_OK;
   hipStream_t s = (hipStream_t)stream;
+  // one final amax value per domain
+  const nvfp4::DomGrid given{1, 1, (uint32_t)ndomains(rows, rows_per_domain)};
   if (axis == 1)
-    return from_hip(nvfp4::launch_encode_rows(x, dtype, rows, cols, ld, rows_per_domain, amax, 1, qout(out),
+    return from_hip(nvfp4::launch_encode_rows(x, dtype, rows, cols, ld, rows_per_domain, amax, given, qout(out),
                                               false, 0, s));
-  return from_hip(nvfp4::launch_encode_cols(x, dtype, rows, cols, ld, amax, 1, qout(out), false, 0, s, out->k));
+  return from_hip(nvfp4::launch_encode_cols(x, dtype, rows, cols, ld, amax, given, qout(out), false, 0, s, out->k));
 }
 
 static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int axis,
@@ -178,21 +180,21 @@ static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, i
   hipStream_t s = (hipStream_t)stream;
   float* parts = static_cast<float*>(ws);
   hipError_t e;
-  uint32_t np;
+  nvfp4::DomGrid pg;
   if (axis == 1 || (!rht && cols % 16 == 0)) {
     // Without the transform the amax does not depend on the block direction,
     // and the row pass covers every column when they fill whole 16-element
     // pieces.  Axis 0 accepts any column count: then the column pass, which
     // handles the right edge, takes the amax.
-    np = nvfp4::amax_parts_rows(rows, cols, 0);
-    e = nvfp4::launch_amax_parts_rows(x, dtype, rows, cols, ld, 0, parts, np, rht, mask, s);
+    pg = nvfp4::amax_grid_rows(rows, cols, 0);
+    e = nvfp4::launch_amax_parts_rows(x, dtype, rows, cols, ld, 0, parts, pg, rht, mask, s);
   } else {
-    np = nvfp4::amax_parts_cols(rows, cols);
-    e = nvfp4::launch_amax_parts_cols(x, dtype, rows, cols, ld, parts, np, rht, mask, s);
+    pg = nvfp4::amax_grid_cols(rows, cols);
+    e = nvfp4::launch_amax_parts_cols(x, dtype, rows, cols, ld, parts, pg, rht, mask, s);
   }
   if (e != hipSuccess) return NVFP4_EHIP;
-  if (axis == 1) e = nvfp4::launch_encode_rows(x, dtype, rows, cols, ld, 0, parts, np, qout(out), rht, mask, s);
-  else e = nvfp4::launch_encode_cols(x, dtype, rows, cols, ld, parts, np, qout(out), rht, mask, s, out->k);
+  if (axis == 1) e = nvfp4::launch_encode_rows(x, dtype, rows, cols, ld, 0, parts, pg, qout(out), rht, mask, s);
+  else e = nvfp4::launch_encode_cols(x, dtype, rows, cols, ld, parts, pg, qout(out), rht, mask, s, out->k);
   return from_hip(e);
 }
 
@@ -261,11 +263,11 @@ static int kv_quant_impl(const void* kv, int64_t frames, int64_t tokens, int64_t
   hipStream_t s = (hipStream_t)stream;
   const int64_t rpd = (frame_block < frames ? frame_block : frames) * tokens * heads;  // <= rows
   float* parts = static_cast<float*>(ws);
-  const uint32_t np = nvfp4::amax_parts_rows(rows, head_dim, rpd);
-  if (nvfp4::launch_amax_parts_rows(kv, NVFP4_BF16, rows, head_dim, head_dim, rpd, parts, np, false, 0, s) !=
+  const nvfp4::DomGrid pg = nvfp4::amax_grid_rows(rows, head_dim, rpd);
+  if (nvfp4::launch_amax_parts_rows(kv, NVFP4_BF16, rows, head_dim, head_dim, rpd, parts, pg, false, 0, s) !=
       hipSuccess)
     return NVFP4_EHIP;
-  return from_hip(nvfp4::launch_encode_rows(kv, NVFP4_BF16, rows, head_dim, head_dim, rpd, parts, np,
+  return from_hip(nvfp4::launch_encode_rows(kv, NVFP4_BF16, rows, head_dim, head_dim, rpd, parts, pg,
                                             qout(out), false, 0, s, four_over_six));
 }
 

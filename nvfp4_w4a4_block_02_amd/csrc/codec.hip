@@ -15,7 +15,12 @@
 //   * the domain amax is reduced without same-address atomics: each
 //     workgroup of the amax pass writes one partial maximum, and every
 //     workgroup of the encode pass reduces its domain's partials (at most
-//     kMaxParts floats, an L2 hit) before it starts;
+//     kMaxParts floats, an L2 hit) before it encodes;
+//   * the amax pass reads with temporal loads so that the encode pass's
+//     second read of a tensor that fits the Infinity Cache comes from there;
+//     the encode pass, the last reader, loads and stores non-temporally;
+//   * multi-domain passes (the KV frame blocks) run on one flat grid with
+//     workgroups in proportion to each domain's size;
 //   * column mode (blocks running down the columns, output stored
 //     transposed): each thread loads a 4-column chunk from 16 consecutive
 //     rows, i.e. four whole blocks, straight into registers; only the
@@ -58,73 +63,90 @@ __device__ __forceinline__ float reduce_parts(const float* __restrict__ parts, i
 }
 
 // ---------------------------------------------------------------------------
-// Step 1, row layout: partial amax of each row domain.  Grid (P, ndom); the
-// workgroup (x, d) writes parts[d * P + x].  Two 16-element blocks per
-// iteration keep four 16-byte loads in flight per thread (bf16).
+// Step 1, row layout: partial amax of each row domain.  Workgroup x of domain
+// d writes parts[d * grid.full + x] (grid.last partials for the last
+// domain).  A thread loads U 16-element blocks at a time (all its loads in
+// flight together: 8 x 16 bytes for bf16).  The loads are temporal: the
+// encode pass reads the same tensor right after, and a tensor that fits the
+// 256 MB Infinity Cache is then served from it (a 65 MB KV tensor: amax +
+// encode 33 -> 28 us; with non-temporal loads here the second read came
+// from HBM).
 template <int DT, bool RHT>
 __global__ __launch_bounds__(kThreads) void amax_rows_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, int64_t rpd,
-    float* __restrict__ parts, uint32_t mask) {
-  const int64_t r0 = (int64_t)blockIdx.y * rpd;
+    float* __restrict__ parts, uint32_t mask, DomGrid dg) {
+  constexpr int U = DT == 1 ? 4 : 2;
+  uint32_t d, wx, nw;
+  dg.locate(blockIdx.x, d, wx, nw);
+  const int64_t r0 = (int64_t)d * rpd;
   const int64_t r1 = rows < r0 + rpd ? rows : r0 + rpd;
   const uint32_t bpr = (uint32_t)(cols / kBlock);
   const uint32_t nblk = (uint32_t)((r1 - r0) * bpr);
   const bool contig = (ld == cols);
   const int64_t base = r0 * ld;
-  const uint32_t stride = gridDim.x * kThreads;
+  const uint32_t stride = nw * kThreads;
   auto offset = [&](uint32_t i) -> int64_t {
     if (contig) return base + (int64_t)i * kBlock;
     const uint32_t r = i / bpr, cb = i - r * bpr;
     return base + (int64_t)r * ld + (int64_t)cb * kBlock;
   };
   float m = 0.0f;
-  uint32_t i = blockIdx.x * kThreads + threadIdx.x;
-  for (; i + stride < nblk; i += 2 * stride) {
-    float v[16], w[16];
-    load16<DT>(x, offset(i), v);
-    load16<DT>(x, offset(i + stride), w);
-    if constexpr (RHT) { rht16(v, mask); rht16(w, mask); }
+  uint32_t i = wx * kThreads + threadIdx.x;
+  for (; i + (U - 1) * stride < nblk; i += U * stride) {
+    float v[U][16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) m = fmaxf(m, fmaxf(fabsf(v[j]), fabsf(w[j])));
+    for (int u = 0; u < U; ++u) load16<DT, false>(x, offset(i + u * stride), v[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if constexpr (RHT) rht16(v[u], mask);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[u][j]));
+    }
   }
-  if (i < nblk) {
+  for (; i < nblk; i += stride) {
     float v[16];
-    load16<DT>(x, offset(i), v);
+    load16<DT, false>(x, offset(i), v);
     if constexpr (RHT) rht16(v, mask);
 #pragma unroll
     for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[j]));
   }
   m = workgroup_max(m);
-  if (threadIdx.x == 0) parts[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = m;
+  if (threadIdx.x == 0) parts[(int64_t)d * dg.full + wx] = m;
 }
 
 // ---------------------------------------------------------------------------
-// Steps 2-6, row layout (axis 1).  Grid (G, ndom).  Block i of domain d is
-// global block gi = d * rpd * bpr + i: elements [16 * (gi % bpr), +16) of row
-// gi / bpr; its codes are bytes [8 gi, 8 gi + 8) and its scale is byte gi of
-// the contiguous outputs.  `parts` holds `nparts` partial maxima per domain.
+// Steps 2-6, row layout (axis 1), over a flat grid of domains (DomGrid).
+// Block i of domain d is global block gi = d * rpd * bpr + i: elements
+// [16 * (gi % bpr), +16) of row gi / bpr; its codes are bytes [8 gi, 8 gi + 8)
+// and its scale is byte gi of the contiguous outputs.
 //
 // FO6: Four Over Six encoder (tailorednewshub.com, "Inferencia W4A4 NVFP4":
 // adaptive scale selection for the KV cache).  Each block is encoded twice,
 // with the scale mapping its maximum to 6 and to 4, and the candidate with
 // the strictly smaller squared decode error (block_sq_error) is stored;
 // ties keep the core recipe.
+//
+// In the core recipe the first blocks' loads are issued before the domain's
+// partial maxima are reduced: the data loads do not depend on the amax, so
+// the two latencies overlap instead of adding up.  `pdg` is the grid of the
+// amax pass that
+// wrote `parts` (pdg.full partials per full domain, pdg.last for the last;
+// full = last = 1 for final amax values), `dg` the grid of this pass.
 template <int DT, bool RHT, bool FO6>
 __global__ __launch_bounds__(kThreads) void encode_rows_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, int64_t rpd,
-    const float* __restrict__ parts, int nparts, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, float* __restrict__ tscale, uint32_t mask) {
-  const uint32_t d = blockIdx.y;
-  const float A = reduce_parts(parts + (int64_t)d * nparts, nparts);
-  const float S = A / kGlobalMax;
-  if (blockIdx.x == 0 && threadIdx.x == 0) tscale[d] = S;
+    const float* __restrict__ parts, DomGrid pdg, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ tscale, uint32_t mask, DomGrid dg) {
+  uint32_t d, wx, nw;
+  dg.locate(blockIdx.x, d, wx, nw);
   const int64_t r0 = (int64_t)d * rpd;
   const int64_t r1 = rows < r0 + rpd ? rows : r0 + rpd;
   const uint32_t bpr = (uint32_t)(cols / kBlock);
   const uint32_t nblk = (uint32_t)((r1 - r0) * bpr);
   const int64_t gbase = r0 * bpr;  // first global block of the domain
   const bool contig = (ld == cols);
-  const uint32_t stride = gridDim.x * kThreads;
+  const uint32_t stride = nw * kThreads;
+  float S = 0.0f;  // the domain's tensor scale, set once its partial maxima are reduced
   auto encode_one = [&](uint32_t i, const float (&vin)[16]) {
     float v[16];
 #pragma unroll
@@ -154,16 +176,30 @@ __global__ __launch_bounds__(kThreads) void encode_rows_kernel(
     const uint32_t r = i / bpr, cb = i - r * bpr;
     return (r0 + r) * ld + (int64_t)cb * kBlock;
   };
-  uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+  uint32_t i = wx * kThreads + threadIdx.x;
+  float v[16], w[16];
+  // the core recipe issues its first loads before the partial maxima are
+  // reduced; the heavier Four Over Six encode runs faster without that
+  // (measured 73 vs 78 us for the K+V pair)
+  const bool h0 = !FO6 && i < nblk, h1 = !FO6 && i + stride < nblk;
+  if (h0) load16<DT>(x, offset(i), v);
+  if (h1) load16<DT>(x, offset(i + stride), w);
+  {
+    const uint32_t np = d + 1 < pdg.ndom ? pdg.full : pdg.last;
+    const float A = reduce_parts(parts + (int64_t)d * pdg.full, (int)np);
+    S = A / kGlobalMax;
+    if (wx == 0 && threadIdx.x == 0) tscale[d] = S;
+  }
+  if (h0) encode_one(i, v);
+  if (h1) encode_one(i + stride, w);
+  if (!FO6) i += 2 * stride;
   for (; i + stride < nblk; i += 2 * stride) {
-    float v[16], w[16];
     load16<DT>(x, offset(i), v);
     load16<DT>(x, offset(i + stride), w);
     encode_one(i, v);
     encode_one(i + stride, w);
   }
   if (i < nblk) {
-    float v[16];
     load16<DT>(x, offset(i), v);
     encode_one(i, v);
   }
@@ -219,55 +255,74 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(
   // the per-thread writes and the per-column reads spread over the banks.
   __shared__ u32x2_t ocodes[AMAX_ONLY ? 1 : kColRB][kColTC + 1];
   __shared__ uint8_t oscale[AMAX_ONLY ? 1 : kColRB][kColTC + 4];
+  const int64_t nbc = out_k / kBlock;              // blocks per output row (>= rows / 16)
+  const uint32_t ntr = cdiv(rows, kColTR), ntc = cdiv(cols, kColTC);
+  const uint32_t ntiles = ntr * ntc;
+  const int t = threadIdx.x, q = t % kColCH, rb = t / kColCH;
+  struct Geo {
+    int64_t k0, c0, r0, cq;
+    int nb;
+    bool active;
+  };
+  auto geo = [&](uint32_t tl) {
+    Geo g;
+    const int64_t tr = tl / ntc, tc = tl - tr * ntc;
+    g.k0 = tr * kColTR;
+    g.c0 = tc * kColTC;
+    g.nb = (int)((rows - g.k0) / kBlock < kColRB ? (rows - g.k0) / kBlock : kColRB);  // row blocks present
+    g.r0 = g.k0 + (int64_t)rb * kBlock;
+    g.cq = g.c0 + (int64_t)q * kColCPC;
+    g.active = rb < g.nb && g.cq < cols;
+    return g;
+  };
+  // This thread's 16 rows x 4 columns of tile tl.
+  auto load_tile = [&](const Geo& g, ColChunk<DT> (&raw)[kBlock]) {
+    if (!g.active) return;
+    if (g.cq + kColCPC <= cols) {
+#pragma unroll
+      for (int i = 0; i < kBlock; ++i) {
+        const int64_t off = (g.r0 + i) * ld + g.cq;
+        // temporal in the amax pass (the encode pass re-reads the tile)
+        if constexpr (DT == 1)
+          raw[i].v = load_hint<!AMAX_ONLY>(reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(x) + off));
+        else
+          raw[i].v = load_hint<!AMAX_ONLY>(reinterpret_cast<const float4_t*>(static_cast<const float*>(x) + off));
+      }
+    } else {  // right edge: columns past `cols` read as 0 (their blocks are skipped)
+#pragma unroll
+      for (int i = 0; i < kBlock; ++i) {
+        const int64_t off = (g.r0 + i) * ld + g.cq;
+        float e[kColCPC];
+#pragma unroll
+        for (int j = 0; j < kColCPC; ++j) e[j] = g.cq + j < cols ? load1<DT>(x, off + j) : 0.0f;
+        if constexpr (DT == 1) {
+          raw[i].v = u32x2_t{(__float_as_uint(e[0]) >> 16) | (__float_as_uint(e[1]) & 0xFFFF0000u),
+                             (__float_as_uint(e[2]) >> 16) | (__float_as_uint(e[3]) & 0xFFFF0000u)};
+        } else {
+          raw[i].v = float4_t{e[0], e[1], e[2], e[3]};
+        }
+      }
+    }
+  };
+  // The first tile's loads go out before the partial maxima are reduced
+  // (they do not depend on the amax); every later tile's loads go out right
+  // after the previous tile's arithmetic, ahead of its stores.
+  ColChunk<DT> raw[kBlock];
+  uint32_t tl = blockIdx.x;
+  if (tl < ntiles) load_tile(geo(tl), raw);
   float S = 0.0f;
   if constexpr (!AMAX_ONLY) {
     S = reduce_parts(parts_in, nparts_in) / kGlobalMax;
     if (blockIdx.x == 0 && threadIdx.x == 0) tscale[0] = S;
   }
-  const int64_t nbc = out_k / kBlock;              // blocks per output row (>= rows / 16)
-  const uint32_t ntr = cdiv(rows, kColTR), ntc = cdiv(cols, kColTC);
-  const uint32_t ntiles = ntr * ntc;
-  const int t = threadIdx.x, q = t % kColCH, rb = t / kColCH;
   float m = 0.0f;
-  for (uint32_t tl = blockIdx.x; tl < ntiles; tl += gridDim.x) {
-    const int64_t tr = tl / ntc, tc = tl - tr * ntc;
-    const int64_t k0 = tr * kColTR, c0 = tc * kColTC;
-    const int nb = (int)((rows - k0) / kBlock < kColRB ? (rows - k0) / kBlock : kColRB);  // row blocks present
-    const int64_t r0 = k0 + (int64_t)rb * kBlock;
-    const int64_t cq = c0 + (int64_t)q * kColCPC;
-    const bool active = rb < nb && cq < cols;
-    ColChunk<DT> raw[kBlock];
-    if (active) {
-      if (cq + kColCPC <= cols) {
-#pragma unroll
-        for (int i = 0; i < kBlock; ++i) {
-          const int64_t off = (r0 + i) * ld + cq;
-          if constexpr (DT == 1)
-            raw[i].v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(x) + off));
-          else
-            raw[i].v = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(static_cast<const float*>(x) + off));
-        }
-      } else {  // right edge: columns past `cols` read as 0 (their blocks are skipped)
-#pragma unroll
-        for (int i = 0; i < kBlock; ++i) {
-          const int64_t off = (r0 + i) * ld + cq;
-          float e[kColCPC];
-#pragma unroll
-          for (int j = 0; j < kColCPC; ++j) e[j] = cq + j < cols ? load1<DT>(x, off + j) : 0.0f;
-          if constexpr (DT == 1) {
-            raw[i].v = u32x2_t{(__float_as_uint(e[0]) >> 16) | (__float_as_uint(e[1]) & 0xFFFF0000u),
-                               (__float_as_uint(e[2]) >> 16) | (__float_as_uint(e[3]) & 0xFFFF0000u)};
-          } else {
-            raw[i].v = float4_t{e[0], e[1], e[2], e[3]};
-          }
-        }
-      }
-    }
+  for (; tl < ntiles; tl += gridDim.x) {
+    const Geo g = geo(tl);
     if constexpr (!AMAX_ONLY) __syncthreads();  // the previous tile's output is written out
-    if (active) {
+    if (g.active) {
 #pragma unroll
       for (int j = 0; j < kColCPC; ++j) {
-        if (cq + j >= cols) break;
+        if (g.cq + j >= cols) break;
         float v[kBlock];
 #pragma unroll
         for (int i = 0; i < kBlock; ++i) v[i] = chunk_elem<DT>(raw[i], j);
@@ -285,6 +340,7 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(
         }
       }
     }
+    if (tl + gridDim.x < ntiles) load_tile(geo(tl + gridDim.x), raw);
     if constexpr (!AMAX_ONLY) {
       __syncthreads();
       // Consecutive threads write consecutive blocks of one output row.
@@ -292,8 +348,8 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(
       for (int h = 0; h < kColTC * kColRB / kThreads; ++h) {
         const int p = t + kThreads * h;
         const int col = p / kColRB, b = p % kColRB;
-        if (b < nb && c0 + col < cols) {
-          const int64_t ob = (c0 + col) * nbc + k0 / kBlock + b;  // block index in the output
+        if (b < g.nb && g.c0 + col < cols) {
+          const int64_t ob = (g.c0 + col) * nbc + g.k0 / kBlock + b;  // block index in the output
           reinterpret_cast<u32x2_t*>(codes)[ob] = ocodes[b][col];
           scales[ob] = oscale[b][col];
         }
@@ -386,10 +442,11 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
   }
 }
 
-__global__ __launch_bounds__(kThreads) void reduce_parts_kernel(const float* __restrict__ parts, int nparts,
+__global__ __launch_bounds__(kThreads) void reduce_parts_kernel(const float* __restrict__ parts, DomGrid pg,
                                                                  float* __restrict__ amax) {
-  const float m = reduce_parts(parts + (int64_t)blockIdx.x * nparts, nparts);
-  if (threadIdx.x == 0) amax[blockIdx.x] = m;
+  const uint32_t d = blockIdx.x;
+  const float m = reduce_parts(parts + (int64_t)d * pg.full, (int)(d + 1 < pg.ndom ? pg.full : pg.last));
+  if (threadIdx.x == 0) amax[d] = m;
 }
 
 // Partial-max workgroups for `nblk` 16-element blocks: about 4 blocks per
@@ -401,14 +458,24 @@ inline uint32_t parts_for(int64_t nblk) {
   return (uint32_t)(p < kMaxParts ? p : kMaxParts);
 }
 
-// Encode workgroups per domain: two blocks per thread per iteration, at most
-// 256 CUs x 16 workgroups over all domains.
-inline uint32_t encode_grid(int64_t nblk, int64_t ndom) {
+// Encode workgroups for a domain of `nblk` blocks: two blocks per thread per
+// iteration, at most 256 CUs x 16 workgroups over all `ndom` domains.
+inline uint32_t encode_count(int64_t nblk, int64_t ndom) {
   int64_t g = (nblk + 2 * kThreads - 1) / (2 * kThreads);
   const int64_t cap = (4096 + ndom - 1) / ndom;
   if (g > cap) g = cap;
   return (uint32_t)(g < 1 ? 1 : g);
 }
+
+// Rows per domain as the kernels take it (0 or more than `rows`: one domain),
+// the domain count and the row count of the last domain.
+inline void domains(int64_t rows, int64_t& rpd, int64_t& ndom, int64_t& last_rows) {
+  if (rpd <= 0 || rpd > rows) rpd = rows;
+  ndom = (rows + rpd - 1) / rpd;
+  last_rows = rows - (ndom - 1) * rpd;
+}
+
+inline unsigned total(const DomGrid& g) { return (g.ndom - 1) * g.full + g.last; }
 
 }  // namespace
 
@@ -419,27 +486,29 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_parts(const float* parts, uint32_t nparts, int64_t ndom, float* amax, hipStream_t s) {
-  reduce_parts_kernel<<<(unsigned)ndom, kThreads, 0, s>>>(parts, (int)nparts, amax);
+hipError_t launch_reduce_parts(const float* parts, DomGrid pg, float* amax, hipStream_t s) {
+  reduce_parts_kernel<<<pg.ndom, kThreads, 0, s>>>(parts, pg, amax);
   return hipGetLastError();
 }
 
-uint32_t amax_parts_rows(int64_t rows, int64_t cols, int64_t rpd) {
-  if (rpd <= 0 || rpd > rows) rpd = rows;
-  return parts_for(rpd * (cols / kBlock));
+DomGrid amax_grid_rows(int64_t rows, int64_t cols, int64_t rpd) {
+  int64_t nd, last;
+  domains(rows, rpd, nd, last);
+  return DomGrid{parts_for(rpd * (cols / kBlock)), parts_for(last * (cols / kBlock)), (uint32_t)nd};
 }
 
-uint32_t amax_parts_cols(int64_t rows, int64_t cols) {
+DomGrid amax_grid_cols(int64_t rows, int64_t cols) {
   const int64_t tiles = (int64_t)cdiv(rows, kColTR) * cdiv(cols, kColTC);
-  return (uint32_t)(tiles < kMaxParts ? (tiles < 1 ? 1 : tiles) : kMaxParts);
+  const uint32_t n = (uint32_t)(tiles < kMaxParts ? (tiles < 1 ? 1 : tiles) : kMaxParts);
+  return DomGrid{n, n, 1};
 }
 
 hipError_t launch_amax_parts_rows(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
-                                  int64_t rpd, float* parts, uint32_t nparts, bool rht, uint32_t mask,
+                                  int64_t rpd, float* parts, DomGrid pg, bool rht, uint32_t mask,
                                   hipStream_t s) {
-  if (rpd <= 0 || rpd > rows) rpd = rows;
-  const dim3 grid(nparts, (unsigned)((rows + rpd - 1) / rpd));
-#define NVFP4_AMAX(D, R) amax_rows_kernel<D, R><<<grid, kThreads, 0, s>>>(x, rows, cols, ld, rpd, parts, mask)
+  int64_t nd, last;
+  domains(rows, rpd, nd, last);
+#define NVFP4_AMAX(D, R) amax_rows_kernel<D, R><<<total(pg), kThreads, 0, s>>>(x, rows, cols, ld, rpd, parts, mask, pg)
   if (dt == 0) { if (rht) NVFP4_AMAX(0, true); else NVFP4_AMAX(0, false); }
   else { if (rht) NVFP4_AMAX(1, true); else NVFP4_AMAX(1, false); }
 #undef NVFP4_AMAX
@@ -447,9 +516,9 @@ hipError_t launch_amax_parts_rows(const void* x, int dt, int64_t rows, int64_t c
 }
 
 hipError_t launch_amax_parts_cols(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
-                                  float* parts, uint32_t nparts, bool rht, uint32_t mask, hipStream_t s) {
+                                  float* parts, DomGrid pg, bool rht, uint32_t mask, hipStream_t s) {
 #define NVFP4_CAMAX(D, R)                                                                        \
-  cols_kernel<D, R, true><<<nparts, kThreads, 0, s>>>(x, rows, cols, ld, nullptr, 0, parts, \
+  cols_kernel<D, R, true><<<pg.full, kThreads, 0, s>>>(x, rows, cols, ld, nullptr, 0, parts, \
                                                             nullptr, nullptr, nullptr, mask, rows)
   if (dt == 0) { if (rht) NVFP4_CAMAX(0, true); else NVFP4_CAMAX(0, false); }
   else { if (rht) NVFP4_CAMAX(1, true); else NVFP4_CAMAX(1, false); }
@@ -458,14 +527,14 @@ hipError_t launch_amax_parts_cols(const void* x, int dt, int64_t rows, int64_t c
 }
 
 hipError_t launch_encode_rows(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
-                              int64_t rpd, const float* parts, uint32_t nparts, QOut out, bool rht,
+                              int64_t rpd, const float* parts, DomGrid pg, QOut out, bool rht,
                               uint32_t mask, hipStream_t s, bool four_over_six) {
-  if (rpd <= 0 || rpd > rows) rpd = rows;
-  const int64_t ndom = (rows + rpd - 1) / rpd;
-  const dim3 grid(encode_grid(rpd * (cols / kBlock), ndom), (unsigned)ndom);
-#define NVFP4_ENC_ROWS(D, R, F)                                                                       \
-  encode_rows_kernel<D, R, F><<<grid, kThreads, 0, s>>>(x, rows, cols, ld, rpd, parts, (int)nparts,  \
-                                                        out.codes, out.scales, out.tscale, mask)
+  int64_t nd, last;
+  domains(rows, rpd, nd, last);
+  const DomGrid eg{encode_count(rpd * (cols / kBlock), nd), encode_count(last * (cols / kBlock), nd), (uint32_t)nd};
+#define NVFP4_ENC_ROWS(D, R, F)                                                                      \
+  encode_rows_kernel<D, R, F><<<total(eg), kThreads, 0, s>>>(x, rows, cols, ld, rpd, parts, pg,     \
+                                                             out.codes, out.scales, out.tscale, mask, eg)
   if (four_over_six) {  // no RHT variant: the KV cache is quantized without it
     if (rht) return hipErrorInvalidValue;
     if (dt == 0) NVFP4_ENC_ROWS(0, false, true); else NVFP4_ENC_ROWS(1, false, true);
@@ -479,7 +548,7 @@ hipError_t launch_encode_rows(const void* x, int dt, int64_t rows, int64_t cols,
 }
 
 hipError_t launch_encode_cols(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
-                              const float* parts, uint32_t nparts, QOut out, bool rht, uint32_t mask,
+                              const float* parts, DomGrid pg, QOut out, bool rht, uint32_t mask,
                               hipStream_t s, int64_t out_k) {
   if (out_k < rows) out_k = rows;
   // Same grid as the amax pass: at most kMaxParts workgroups, so that a
@@ -487,7 +556,7 @@ hipError_t launch_encode_cols(const void* x, int dt, int64_t rows, int64_t cols,
   const int64_t tiles = (int64_t)cdiv(rows, kColTR) * cdiv(cols, kColTC);
   const unsigned grid = (unsigned)(tiles < (int64_t)kMaxParts ? tiles : kMaxParts);
 #define NVFP4_ENC_COLS(D, R)                                                                     \
-  cols_kernel<D, R, false><<<grid, kThreads, 0, s>>>(x, rows, cols, ld, parts, (int)nparts, \
+  cols_kernel<D, R, false><<<grid, kThreads, 0, s>>>(x, rows, cols, ld, parts, (int)pg.full, \
                                                           nullptr, out.codes, out.scales,        \
                                                           out.tscale, mask, out_k)
   if (dt == 0) { if (rht) NVFP4_ENC_COLS(0, true); else NVFP4_ENC_COLS(0, false); }

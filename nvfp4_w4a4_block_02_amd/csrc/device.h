@@ -73,26 +73,31 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Load 16 consecutive elements (16-byte aligned) as float32.
-template <int DT>
-__device__ __forceinline__ void load16(const void* __restrict__ base, int64_t elem_off, float (&v)[16]);
-
-template <>
-__device__ __forceinline__ void load16<0>(const void* __restrict__ base, int64_t elem_off, float (&v)[16]) {
-  const float4_t* p = reinterpret_cast<const float4_t*>(static_cast<const float*>(base) + elem_off);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4_t q = __builtin_nontemporal_load(p + i);
-    v[4 * i + 0] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
-  }
+// A 16-byte load, non-temporal (last use of the data: streamed past the
+// caches) or temporal (the data is read again soon, e.g. by the encode pass
+// right after the amax pass: it can then come from the Infinity Cache).
+template <bool NT, typename T>
+__device__ __forceinline__ T load_hint(const T* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
 }
 
-template <>
-__device__ __forceinline__ void load16<1>(const void* __restrict__ base, int64_t elem_off, float (&v)[16]) {
+// Load 16 consecutive elements (16-byte aligned) as float32.
+template <int DT, bool NT = true>
+__device__ __forceinline__ void load16(const void* __restrict__ base, int64_t elem_off, float (&v)[16]) {
+  if constexpr (DT == 0) {
+    const float4_t* p = reinterpret_cast<const float4_t*>(static_cast<const float*>(base) + elem_off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4_t q = load_hint<NT>(p + i);
+      v[4 * i + 0] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+    }
+    return;
+  }
   const u32x4_t* p = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(base) + elem_off);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const u32x4_t q = __builtin_nontemporal_load(p + i);
+    const u32x4_t q = load_hint<NT>(p + i);
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

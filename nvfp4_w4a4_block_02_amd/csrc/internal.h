@@ -21,30 +21,47 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t s);
 // consumers reduce at most kMaxParts of them per domain.
 constexpr uint32_t kMaxParts = 1024;
 
-// Number of partials the amax passes below use for a problem.
-uint32_t amax_parts_rows(int64_t rows, int64_t cols, int64_t rows_per_domain);
-uint32_t amax_parts_cols(int64_t rows, int64_t cols);
+// Workgroups of a pass over row domains (the amax pass, which writes one
+// partial maximum per workgroup, or the encode pass): every domain but the
+// last has rows_per_domain rows and gets `full` workgroups, the last
+// (possibly shorter) one gets `last`, on one flat grid of
+// (ndom - 1) * full + last workgroups.  The partial maxima of domain d are
+// parts[d * full + x], x < (d + 1 < ndom ? full : last).  Final per-domain
+// amax values are the case full = last = 1.
+struct DomGrid {
+  uint32_t full, last, ndom;
+  __host__ __device__ inline void locate(uint32_t g, uint32_t& d, uint32_t& x, uint32_t& n) const {
+    d = g / full;
+    if (d >= ndom) d = ndom - 1;
+    x = g - d * full;
+    n = d + 1 < ndom ? full : last;
+  }
+};
+
+// Partial-maximum grids the amax passes below use for a problem.
+DomGrid amax_grid_rows(int64_t rows, int64_t cols, int64_t rows_per_domain);
+DomGrid amax_grid_cols(int64_t rows, int64_t cols);
 
 // Step 1: partial amax per domain, row layout (also used for axis 0 without
-// the transform, where the amax does not depend on the block direction);
-// parts[d * nparts + w].
+// the transform when cols % 16 == 0, where the amax does not depend on the
+// block direction).
 hipError_t launch_amax_parts_rows(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
-                                  int64_t rows_per_domain, float* parts, uint32_t nparts, bool rht,
+                                  int64_t rows_per_domain, float* parts, DomGrid pg, bool rht,
                                   uint32_t mask, hipStream_t s);
-// Step 1 for blocks running down the columns (one domain), needed with the RHT.
+// Step 1 for blocks running down the columns (one domain).
 hipError_t launch_amax_parts_cols(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
-                                  float* parts, uint32_t nparts, bool rht, uint32_t mask, hipStream_t s);
-// Reduce `nparts` partials per domain into amax[ndom].
-hipError_t launch_reduce_parts(const float* parts, uint32_t nparts, int64_t ndom, float* amax, hipStream_t s);
+                                  float* parts, DomGrid pg, bool rht, uint32_t mask, hipStream_t s);
+// Reduce the partials of every domain into amax[ndom].
+hipError_t launch_reduce_parts(const float* parts, DomGrid pg, float* amax, hipStream_t s);
 
-// Steps 2-6 from per-domain partial maxima (nparts = 1: final amax values).
+// Steps 2-6 from per-domain partial maxima laid out as `pg` says.
 // four_over_six: Four Over Six block-scale selection (not combined with rht).
 hipError_t launch_encode_rows(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
-                              int64_t rows_per_domain, const float* parts, uint32_t nparts, QOut out,
+                              int64_t rows_per_domain, const float* parts, DomGrid pg, QOut out,
                               bool rht, uint32_t mask, hipStream_t s, bool four_over_six = false);
 // out_k: length of the output rows (>= rows; blocks past rows are zeroed).
 hipError_t launch_encode_cols(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
-                              const float* parts, uint32_t nparts, QOut out, bool rht, uint32_t mask,
+                              const float* parts, DomGrid pg, QOut out, bool rht, uint32_t mask,
                               hipStream_t s, int64_t out_k = 0);
 
 // Step 7.
