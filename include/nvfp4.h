@@ -110,8 +110,11 @@ const char *nvfp4_status_string(int status);
 size_t nvfp4_workspace_bytes(int op, int64_t rows, int64_t cols);
 
 /*
- * Domain amax (step 1 of the recipe): amax[d] = max |x| over the rows of
- * domain d, where domain d is rows [d*rows_per_domain, (d+1)*rows_per_domain)
+ * Domain amax (step 1 of the recipe): the FP32 tensor scale of NVFP4 is
+ * derived from the largest magnitude of its scaling domain (neurohive.io NVFP4
+ * paragraph: a per-tensor scale beside the 16-element block scales; hyper.ai
+ * LongLive-2.0 summary, "方法": one domain per 8-frame block of the KV cache).
+ * amax[d] = max |x| over the rows of domain d, where domain d is rows [d*rows_per_domain, (d+1)*rows_per_domain)
  * (the last domain may be shorter; rows_per_domain = 0 means one domain).
  * x: device [rows][ld] of `dtype`.  amax: device float32
  * [ceil(rows/rows_per_domain)], overwritten.  The maximum is exact and does
@@ -123,7 +126,11 @@ int nvfp4_amax(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
 
 /*
  * Encode (steps 2-6) given each domain's amax: writes codes, block scales
- * and tscale[d] = amax[d] / 2688.
+ * and tscale[d] = amax[d] / 2688 — the E2M1 elements with one FP8 scale per
+ * 16 elements and one FP32 scale per domain of the NVFP4 format (neurohive.io
+ * NVFP4 paragraph; tailorednewshub.com, "Entrenamiento NVFP4").  Split from
+ * nvfp4_quantize so that a caller holding the amax already (the GEMM
+ * epilogue's max |H|, a weight quantized along both dims) skips its pass.
  *   axis = 1: blocks run along cols (x is [rows][cols], K-contiguous); the
  *             output is rows x cols.
  *   axis = 0: blocks run along rows (x's reduction dim is dim 0, as for a
@@ -203,7 +210,8 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtyp
                void *stream);
 
 /*
- * nvfp4_gemm with an explicit tile shape instead of the built-in choice.
+ * nvfp4_gemm with an explicit tile shape instead of the built-in choice (the
+ * same W4A4 GEMM: tailorednewshub.com, "Inferencia W4A4 NVFP4").
  * tile_fa x tile_fb is the number of 32x32 MFMA fragments per wavefront
  * along M x N (a workgroup covers 64*tile_fa x 64*tile_fb outputs); the
  * supported shapes are 2x4, 4x2, 3x3 and 4x4, used when K >= 128 and
@@ -292,8 +300,11 @@ int nvfp4_kv_attention(const void *q, int64_t q_frames, const nvfp4_tensor *k, c
                        int64_t frame_block, void *out, int out_dtype, void *stream);
 
 /*
- * Plain dequantization (decode step), float32 or bf16 output [rows][k],
- * contiguous; rows_per_domain as in nvfp4_amax (0 = one domain).
+ * Plain dequantization, the format's decode x' = f32(e2m1 * s_b) * S
+ * (neurohive.io NVFP4 paragraph: E2M1 values, FP8 block and FP32 tensor
+ * scales; the same decode the KV dequantizer applies, hyper.ai LongLive-2.0
+ * summary, "方法"), float32 or bf16 (round-to-nearest-even) output
+ * [rows][k], contiguous; rows_per_domain as in nvfp4_amax (0 = one domain).
  */
 int nvfp4_dequantize(const nvfp4_tensor *in, int64_t rows_per_domain, void *out,
                      int dtype, void *stream);

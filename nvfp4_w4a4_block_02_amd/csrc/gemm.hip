@@ -37,6 +37,7 @@
 // Fallback kernel (any K % 16 == 0): the same fragments loaded straight into
 // registers with bounds checks; code bytes past K read as 0.
 #include <cmath>
+#include <type_traits>
 
 #include "device.h"
 #include "internal.h"
@@ -140,10 +141,44 @@ __device__ __forceinline__ void compute_tile(const Frags<FA, FB>& t, float16_t (
 // Epilogue: tensor scales, optional GELU, store, optional amax of the stored
 // values.  MFMA 32x32 output layout: lane l, accumulator r holds row
 // (r / 4) * 8 + (l / 32) * 4 + r % 4, column l % 32 of the fragment.
+//
+// A sub-tile wholly inside C takes a branch-free path: one base address per
+// lane, the row offsets (uniform multiples of ldc) added per accumulator row
+// and the column fragments as immediate store offsets; edge sub-tiles check
+// every element.  Both store the same values.
 template <int FA, int FB, int OUT, int EPI>
 __device__ __forceinline__ void store_tile(const float16_t (&acc)[FA][FB], float sab, int m0, int n0, int li, int hh,
                                            int M, int N, void* __restrict__ c, int64_t ldc, float* __restrict__ amax_out) {
+  using T = typename std::conditional<OUT == 0, float, uint16_t>::type;
   float mx = 0.0f;
+  if (m0 + 32 * FA <= M && n0 + 32 * FB <= N) {
+    T* const base = static_cast<T*>(c) + (int64_t)(m0 + hh * 4) * ldc + n0 + li;
+#pragma unroll
+    for (int i = 0; i < FA; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        T* const p = base + (int64_t)(32 * i + (r >> 2) * 8 + (r & 3)) * ldc;
+#pragma unroll
+        for (int j = 0; j < FB; ++j) {
+          float v = acc[i][j][r] * sab;
+          if constexpr (EPI == 1) v = gelu_tanh(v);
+          if constexpr (OUT == 0) {
+            p[32 * j] = v;
+          } else {
+            const uint32_t hb = f32_to_bf16_rne(v);
+            p[32 * j] = (uint16_t)hb;
+            v = bf16_to_f32(hb);
+          }
+          mx = fmaxf(mx, fabsf(v));
+        }
+      }
+    }
+    if (amax_out != nullptr) {
+      mx = wave_max(mx);
+      if ((threadIdx.x & 63) == 0 && mx > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(amax_out), __float_as_uint(mx));
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FA; ++i) {
 #pragma unroll
