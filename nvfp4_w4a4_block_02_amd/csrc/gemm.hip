@@ -408,7 +408,8 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
   static_assert(3 * L < 64, "three tiles of loads must fit the vmcnt counter");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * STAGE];
 
-  const int l = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS destinations in SGPRs
   const int li = l & 31, hh = l >> 5;
   const int tiles_n = (N + 64 * FB - 1) / (64 * FB);
   const int tiles_m = (M + 64 * FA - 1) / (64 * FA);
@@ -420,8 +421,13 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
   // Load slots: code loads (2 per fragment) and scale loads (1 per fragment)
   // dealt round-robin over the 4 waves.  Lane l of a code load fetches the
   // 16-byte half q of row (32 f + l % 32), k-half l / 32; rows past M / N are
-  // clamped (computed, never stored).
-  const uint8_t* src[L];
+  // clamped (computed, never stored).  The address of a load is a uniform
+  // base (the operand, advanced per K-tile) plus a 32-bit lane offset (the
+  // host takes this path only for operands below 2^31 bytes), so it goes out
+  // with a scalar base and the LDS destination is uniform too: no per-load
+  // 64-bit vector arithmetic.
+  const uint8_t* base[L];
+  uint32_t off[L];
   int dst[L];
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
@@ -429,7 +435,8 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
     const bool isA = i < 2 * NFA;
     const int ii = isA ? i : i - 2 * NFA, f = ii >> 1, q = ii & 1;
     const int row = isA ? min(mwg + 32 * f + li, M - 1) : min(nwg + 32 * f + li, N - 1);
-    src[j] = (isA ? ac : bc) + (int64_t)row * cpitch + 32 * hh + 16 * q;
+    base[j] = isA ? ac : bc;
+    off[j] = (uint32_t)row * (uint32_t)cpitch + 32 * hh + 16 * q;
     dst[j] = (isA ? 0 : OFF_B) + (2 * f + q) * 1024;
   }
 #pragma unroll
@@ -438,15 +445,18 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
     const bool isA = i < NFA;
     const int f = isA ? i : i - NFA;
     const int row = isA ? min(mwg + 32 * f + li, M - 1) : min(nwg + 32 * f + li, N - 1);
-    src[CPW + j] = (isA ? as : bs) + (int64_t)row * spitch + 4 * hh;
+    base[CPW + j] = isA ? as : bs;
+    off[CPW + j] = (uint32_t)row * (uint32_t)spitch + 4 * hh;
     dst[CPW + j] = (isA ? OFF_SA : OFF_SB) + f * 256;
   }
   // Load j of tile `tile` into the stage at `st`.
   auto load = [&](int j, int tile, uint8_t* st) {
     if (j < CPW)
-      __builtin_amdgcn_global_load_lds((gvoid_t*)(src[j] + (int64_t)tile * (kKT / 2)), (lvoid_t*)(st + dst[j]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gvoid_t*)(base[j] + (int64_t)tile * (kKT / 2) + off[j]), (lvoid_t*)(st + dst[j]),
+                                       16, 0, 0);
     else if (j < L)
-      __builtin_amdgcn_global_load_lds((gvoid_t*)(src[j] + (int64_t)tile * (kKT / 16)), (lvoid_t*)(st + dst[j]), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((gvoid_t*)(base[j] + (int64_t)tile * (kKT / 16) + off[j]), (lvoid_t*)(st + dst[j]),
+                                       4, 0, 0);
   };
 
   const int wy = wave >> 1, wx = wave & 1;
@@ -666,7 +676,8 @@ hipError_t launch_gemm(QOut a, QOut b, int64_t m, int64_t n, int64_t k, void* c,
   // aligned and every scale row 4-byte aligned (the direct-to-LDS loads need
   // both); a remainder of 64 goes through the checked tail tile.
   const bool lds_path = (k >= kKT) && (k % 64 == 0) && ((uintptr_t)a.codes % 16 == 0) && ((uintptr_t)b.codes % 16 == 0) &&
-                        ((uintptr_t)a.scales % 4 == 0) && ((uintptr_t)b.scales % 4 == 0);
+                        ((uintptr_t)a.scales % 4 == 0) && ((uintptr_t)b.scales % 4 == 0) &&
+                        m * (k / 2) < ((int64_t)1 << 31) && n * (k / 2) < ((int64_t)1 << 31);  // 32-bit load offsets
   if (lds_path) {
     int fa = tile_fa, fb = tile_fb;
     if (!gemm_tiles_supported(fa, fb)) pick_tiles((int)m, (int)n, fa, fb);
