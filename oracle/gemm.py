@@ -1,4 +1,4 @@
-"""Block-scaled W4A4 GEMM reference, GELU-tanh and the FFN chain.
+"""Block-scaled W4A4 GEMM reference and GELU-tanh.
 
 Test infrastructure only (see the package docstring).
 
@@ -22,7 +22,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codec import QTensor, decode_exact, quantize
+from .codec import QTensor, decode_exact
 
 F32 = np.float32
 
@@ -57,18 +57,3 @@ def gelu_tanh(h) -> np.ndarray:
     u = c * (h + 0.044715 * h ** 3)
     with np.errstate(over="ignore"):
         return h / (1.0 + np.exp(-2.0 * u))
-
-
-def ffn_chain(x: np.ndarray, w1: QTensor, w2: QTensor):
-    """Full-oracle FFN pair: quantize x -> GEMM1 -> GELU -> float32 H ->
-    quantize H (its own global amax) -> GEMM2.
-
-    Returns a dict with every intermediate (float64 GEMM results and bounds,
-    the float32 H and the quantized operands)."""
-    xq = quantize(np.asarray(x, dtype=np.float32))
-    c1, b1 = gemm_ref(xq, w1)
-    h64 = gelu_tanh(c1)
-    h32 = h64.astype(np.float32)
-    hq = quantize(h32)
-    c2, b2 = gemm_ref(hq, w2)
-    return {"xq": xq, "c1": c1, "b1": b1, "h64": h64, "h32": h32, "hq": hq, "c2": c2, "b2": b2}

@@ -124,14 +124,3 @@ def test_gelu_against_high_precision_definition():
     assert np.all(ours[h < -6] != 0.0) and np.all(ref[h < -6] != 0.0)   # the tail is not flushed
     rtol = 2.0 ** -52 * (8 + 4 * np.abs(u))
     assert np.all(np.abs(ours - ref) <= rtol * np.abs(ref) + 1e-320)
-
-
-def test_ffn_chain_wiring():
-    rng = np.random.default_rng(3)
-    x = rng.standard_normal((8, 32)).astype(np.float32)
-    w1 = oracle.quantize((rng.standard_normal((48, 32)) * 0.02).astype(np.float32))
-    w2 = oracle.quantize((rng.standard_normal((32, 48)) * 0.02).astype(np.float32))
-    r = oracle.ffn_chain(x, w1, w2)
-    assert r["c1"].shape == (8, 48) and r["c2"].shape == (8, 32)
-    assert np.array_equal(r["h32"], oracle.gelu_tanh(oracle.gemm_ref(oracle.quantize(x), w1)[0]).astype(np.float32))
-    assert np.array_equal(r["hq"].codes, oracle.quantize(r["h32"]).codes)
