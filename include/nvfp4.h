@@ -214,7 +214,7 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtyp
  * same W4A4 GEMM: tailorednewshub.com, "Inferencia W4A4 NVFP4").
  * tile_fa x tile_fb is the number of 32x32 MFMA fragments per wavefront
  * along M x N (a workgroup covers 64*tile_fa x 64*tile_fb outputs); the
- * supported shapes are 2x4, 4x2, 3x3 and 4x4, used when K >= 128 and
+ * supported shapes are 2x4, 4x2, 3x3, 4x4 and 1x1, used when K >= 128 and
  * K % 64 == 0 (other K always take the bounds-checked 2x4 kernel).  Every
  * shape accumulates each output element in the same order, so results are
  * bit-identical across shapes.  Unsupported shapes return NVFP4_EINVAL.

@@ -631,7 +631,8 @@ void launch_lds(const Args& g, hipStream_t s) {
 
 template <int OUT, int EPI>
 void launch_lds_tiles(int fa, int fb, const Args& g, hipStream_t s) {
-  if (fa == 4 && fb == 4) launch_lds<4, 4, OUT, EPI>(g, s);
+  if (fa == 1 && fb == 1) launch_lds<1, 1, OUT, EPI>(g, s);
+  else if (fa == 4 && fb == 4) launch_lds<4, 4, OUT, EPI>(g, s);
   else if (fa == 3 && fb == 3) launch_lds<3, 3, OUT, EPI>(g, s);
   else if (fa == 4 && fb == 2) launch_lds<4, 2, OUT, EPI>(g, s);
   else launch_lds<2, 4, OUT, EPI>(g, s);
@@ -646,10 +647,12 @@ void launch_checked(const Args& g, hipStream_t s) {
 
 // Tile shape by a small cost model: rounds of 256 workgroups (one per CU) x
 // MFMA work per workgroup / relative efficiency of the shape (bigger
-// fragments amortize the decode over more MFMAs).
+// fragments amortize the decode over more MFMAs).  The 64 x 64 tile (one
+// fragment per wavefront) decodes the most per MFMA but spreads a small
+// output over many CUs, which is what a latency-bound problem needs.
 void pick_tiles(int m, int n, int& fa, int& fb) {
   struct Cand { int fa, fb; double eff; };
-  const Cand cands[] = {{2, 4, 1.0}, {4, 2, 1.0}, {3, 3, 1.05}, {4, 4, 1.15}};
+  const Cand cands[] = {{2, 4, 1.0}, {4, 2, 1.0}, {3, 3, 1.05}, {4, 4, 1.15}, {1, 1, 0.45}};
   double best = 1e300;
   for (const Cand& cd : cands) {
     const long tiles = (long)((m + 64 * cd.fa - 1) / (64 * cd.fa)) * ((n + 64 * cd.fb - 1) / (64 * cd.fb));
@@ -662,7 +665,8 @@ void pick_tiles(int m, int n, int& fa, int& fb) {
 }  // namespace
 
 bool gemm_tiles_supported(int fa, int fb) {
-  return (fa == 2 && fb == 4) || (fa == 4 && fb == 2) || (fa == 3 && fb == 3) || (fa == 4 && fb == 4);
+  return (fa == 2 && fb == 4) || (fa == 4 && fb == 2) || (fa == 3 && fb == 3) || (fa == 4 && fb == 4) ||
+         (fa == 1 && fb == 1);
 }
 
 hipError_t launch_gemm(QOut a, QOut b, int64_t m, int64_t n, int64_t k, void* c, int c_dt,

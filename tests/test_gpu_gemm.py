@@ -53,7 +53,7 @@ def test_gemm_matches_oracle(nv, m, n, k, out):
     assert_gemm_close(c.float().cpu().numpy(), cref, bound, out == "bf16", f"{m}x{n}x{k} {out}")
 
 
-@pytest.mark.parametrize("tiles", [(2, 4), (4, 2), (3, 3), (4, 4)])
+@pytest.mark.parametrize("tiles", [(2, 4), (4, 2), (3, 3), (4, 4), (1, 1)])
 @pytest.mark.parametrize("m,n,k", [(300, 520, 384), (97, 1100, 1280), (1030, 70, 256), (200, 330, 192),
                                    (65, 300, 1344)])
 def test_gemm_every_tile_shape(nv, tiles, m, n, k):
@@ -84,7 +84,8 @@ def test_tile_shapes_are_bit_identical(nv, m, n, k):
     a[rng.random(a.shape) < 0.02] *= 50
     b = (rng.standard_normal((n, k)) * np.exp(rng.uniform(-3, 3, (1, k)))).astype(np.float32)
     ga, gb = nv.quantize(dev_f32(a)), nv.quantize(dev_f32(b))
-    outs = [nv.gemm(ga, gb, out_dtype=torch.float32, tiles=t).cpu().numpy() for t in (None, (2, 4), (4, 2), (3, 3), (4, 4))]
+    outs = [nv.gemm(ga, gb, out_dtype=torch.float32, tiles=t).cpu().numpy()
+            for t in (None, (2, 4), (4, 2), (3, 3), (4, 4), (1, 1))]
     for o in outs[1:]:
         assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
     cref, bound = oracle.gemm_ref(oracle.quantize(a), oracle.quantize(b))
@@ -119,7 +120,7 @@ def test_gemm_into_strided_output(nv):
 
 
 @pytest.mark.parametrize("width", [312, 301])
-@pytest.mark.parametrize("tiles", [(2, 4), (4, 2), (4, 4)])
+@pytest.mark.parametrize("tiles", [(2, 4), (4, 2), (4, 4), (1, 1)])
 def test_gemm_bf16_into_strided_output(nv, width, tiles):
     """bf16 output rows `width` elements apart: whole wavefront sub-tiles go
     through the LDS-staged 16-byte stores when rows are 16-byte aligned
