@@ -203,7 +203,10 @@ int rht16_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t
  * float32).  amax_out: NULL, or a device float that receives max |c| over the
  * stored values (it is reset by the call), so that c can be re-quantized with
  * nvfp4_encode without another pass over it.  ws may be NULL
- * (nvfp4_workspace_bytes(NVFP4_OP_GEMM, ...) is 0).
+ * (nvfp4_workspace_bytes(NVFP4_OP_GEMM, ...) is 0).  The tile shape is
+ * chosen per problem; when the last row of tiles is mostly empty, the call
+ * may run the full tile rows and the remaining rows as two kernels on
+ * `stream` (same values as one kernel; the amax covers both).
  */
 int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtype,
                int64_t ldc, int epilogue, float *amax_out, void *ws, size_t ws_bytes,

@@ -657,16 +657,22 @@ void launch_checked(const Args& g, hipStream_t s) {
 // fragments amortize the decode over more MFMAs).  The 64 x 64 tile (one
 // fragment per wavefront) decodes the most per MFMA but spreads a small
 // output over many CUs, which is what a latency-bound problem needs.
-void pick_tiles(int m, int n, int& fa, int& fb) {
-  struct Cand { int fa, fb; double eff; };
-  const Cand cands[] = {{2, 4, 1.0}, {4, 2, 1.0}, {3, 3, 1.05}, {4, 4, 1.15}, {1, 1, 0.45}};
-  double best = 1e300;
-  for (const Cand& cd : cands) {
-    const long tiles = (long)((m + 64 * cd.fa - 1) / (64 * cd.fa)) * ((n + 64 * cd.fb - 1) / (64 * cd.fb));
-    const long rounds = (tiles + 255) / 256;
-    const double cost = (double)rounds * cd.fa * cd.fb / cd.eff;
-    if (cost < best - 1e-9) { best = cost; fa = cd.fa; fb = cd.fb; }
+struct Cand { int fa, fb; double eff; };
+constexpr Cand kCands[] = {{2, 4, 1.0}, {4, 2, 1.0}, {3, 3, 1.05}, {4, 4, 1.15}, {1, 1, 0.45}};
+
+double tile_cost(int64_t m, int64_t n, const Cand& cd) {
+  const int64_t tiles = ((m + 64 * cd.fa - 1) / (64 * cd.fa)) * ((n + 64 * cd.fb - 1) / (64 * cd.fb));
+  return (double)((tiles + 255) / 256) * cd.fa * cd.fb / cd.eff;
+}
+
+Cand pick_tiles(int64_t m, int64_t n) {
+  Cand best = kCands[0];
+  double bc = 1e300;
+  for (const Cand& cd : kCands) {
+    const double c = tile_cost(m, n, cd);
+    if (c < bc - 1e-9) { bc = c; best = cd; }
   }
+  return best;
 }
 
 }  // namespace
@@ -690,10 +696,39 @@ hipError_t launch_gemm(QOut a, QOut b, int64_t m, int64_t n, int64_t k, void* c,
                         ((uintptr_t)a.scales % 4 == 0) && ((uintptr_t)b.scales % 4 == 0) &&
                         m * (k / 2) < ((int64_t)1 << 31) && n * (k / 2) < ((int64_t)1 << 31);  // 32-bit load offsets
   if (lds_path) {
-    int fa = tile_fa, fb = tile_fb;
-    if (!gemm_tiles_supported(fa, fb)) pick_tiles((int)m, (int)n, fa, fb);
-    if (c_dt == 0) { if (epilogue == 1) launch_lds_tiles<0, 1>(fa, fb, g, s); else launch_lds_tiles<0, 0>(fa, fb, g, s); }
-    else { if (epilogue == 1) launch_lds_tiles<1, 1>(fa, fb, g, s); else launch_lds_tiles<1, 0>(fa, fb, g, s); }
+    auto run = [&](int fa, int fb, const Args& ar) {
+      if (c_dt == 0) { if (epilogue == 1) launch_lds_tiles<0, 1>(fa, fb, ar, s); else launch_lds_tiles<0, 0>(fa, fb, ar, s); }
+      else { if (epilogue == 1) launch_lds_tiles<1, 1>(fa, fb, ar, s); else launch_lds_tiles<1, 0>(fa, fb, ar, s); }
+    };
+    if (gemm_tiles_supported(tile_fa, tile_fb)) {
+      run(tile_fa, tile_fb, g);
+      return hipGetLastError();
+    }
+    const Cand cd = pick_tiles(m, n);
+    // A last row of tiles that is mostly empty can cost a whole extra round
+    // of workgroups (10560 rows in 256-row tiles: 41 full tile rows and one
+    // of 64 rows, 10 rounds of 256 tiles where 9 hold the work).  When the
+    // cost model says so, the full tile rows run as one launch and the
+    // remaining rows as a second launch with tiles fitted to them.  Every
+    // output element is the same whatever tile computes it, so the split
+    // changes no value.
+    const int64_t tm = 64 * cd.fa, full = m / tm, rem = m - full * tm;
+    if (rem > 0 && full > 0) {
+      const Cand rc = pick_tiles(rem, n);
+      if (tile_cost(full * tm, n, cd) + tile_cost(rem, n, rc) < 0.95 * tile_cost(m, n, cd)) {
+        const int64_t m1 = full * tm;
+        Args top = g, bottom = g;
+        top.m = (int)m1;
+        bottom.m = (int)rem;
+        bottom.a.codes = a.codes + m1 * (k / 2);
+        bottom.a.scales = a.scales + m1 * (k / 16);
+        bottom.c = static_cast<uint8_t*>(c) + m1 * ldc * (c_dt == 0 ? 4 : 2);
+        run(cd.fa, cd.fb, top);
+        run(rc.fa, rc.fb, bottom);
+        return hipGetLastError();
+      }
+    }
+    run(cd.fa, cd.fb, g);
   } else {
     if (c_dt == 0) { if (epilogue == 1) launch_checked<0, 1>(g, s); else launch_checked<0, 0>(g, s); }
     else { if (epilogue == 1) launch_checked<1, 1>(g, s); else launch_checked<1, 0>(g, s); }

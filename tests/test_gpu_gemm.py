@@ -93,6 +93,30 @@ def test_tile_shapes_are_bit_identical(nv, m, n, k):
     assert np.any(outs[0] != cref.astype(np.float32))  # the float32 accumulation rounded somewhere
 
 
+def test_split_last_tile_row(nv):
+    """2144 x 8192: the automatic choice (128 x 256 tiles) would leave a last
+    tile row of 96 rows that costs a third round of workgroups, so the 2048
+    full tile rows and the 96 remaining rows run as two launches (the second
+    with 64 x 64 tiles).  The result is bit-identical to one launch with
+    pinned tiles, float32 and the bf16 GELU epilogue with its amax alike, and
+    the rows on both sides of the seam match the float64 oracle."""
+    m, n, k = 2144, 8192, 256
+    log(f"gemm split of the last tile row {m}x{n}x{k}")
+    rng = np.random.default_rng(2144)
+    ga, gb, oa, ob = _operands(nv, rng, m, n, k)
+    auto = nv.gemm(ga, gb, out_dtype=torch.float32).cpu().numpy()
+    pinned = nv.gemm(ga, gb, out_dtype=torch.float32, tiles=(2, 4)).cpu().numpy()
+    assert np.array_equal(auto.view(np.uint32), pinned.view(np.uint32))
+    amax_a, amax_p = torch.empty(1, device="cuda"), torch.empty(1, device="cuda")
+    ha = nv.gemm(ga, gb, out_dtype=torch.bfloat16, epilogue=nv.EPI_GELU_TANH, amax_out=amax_a)
+    hp = nv.gemm(ga, gb, out_dtype=torch.bfloat16, epilogue=nv.EPI_GELU_TANH, amax_out=amax_p, tiles=(2, 4))
+    assert torch.equal(ha.view(torch.int16), hp.view(torch.int16))
+    assert amax_a.item() == amax_p.item() == float(ha.float().abs().max().item())
+    rows = slice(1984, m)
+    cref, bound = oracle.gemm_ref(oa, ob, rows=rows)
+    assert_gemm_close(auto[rows], cref, bound, False, "rows at the seam")
+
+
 def test_gemm_with_an_all_zero_operand(nv):
     """A zero activation tensor quantizes to S = 0; the product is exactly 0
     everywhere (no NaN from 0 * scale paths) and the output amax is 0."""
