@@ -205,6 +205,77 @@ __global__ __launch_bounds__(kThreads) void encode_rows_kernel(
   }
 }
 
+// Float32 encode with four lanes per block (core recipe, no RHT): lane q of a
+// quad holds elements 4q .. 4q+3 of its block, so one 16-byte load per lane
+// reads 1 KiB of consecutive memory per wavefront (with one block per lane,
+// each load instruction touched 64 separate 64-byte pieces).  The block
+// maximum is combined over the quad with two DPP swaps; every lane derives
+// the same scale and converts its four elements into two code bytes.  Codes
+// and scales are the same as those of encode_rows_kernel.
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));  // lane ^ 1
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));  // lane ^ 2
+  return v;
+}
+
+__global__ __launch_bounds__(kThreads) void encode_rows_f32q_kernel(
+    const float* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, int64_t rpd,
+    const float* __restrict__ parts, DomGrid pdg, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ tscale, DomGrid dg) {
+  constexpr uint32_t BPW = kThreads / 4;  // blocks per workgroup sweep
+  uint32_t d, wx, nw;
+  dg.locate(blockIdx.x, d, wx, nw);
+  const int64_t r0 = (int64_t)d * rpd;
+  const int64_t r1 = rows < r0 + rpd ? rows : r0 + rpd;
+  const uint32_t bpr = (uint32_t)(cols / kBlock);
+  const uint32_t nblk = (uint32_t)((r1 - r0) * bpr);
+  const int64_t gbase = r0 * bpr;
+  const bool contig = (ld == cols);
+  const uint32_t stride = nw * BPW;
+  const uint32_t q = threadIdx.x & 3;
+  auto offset = [&](uint32_t i) -> int64_t {
+    if (contig) return r0 * ld + (int64_t)i * kBlock + 4 * q;
+    const uint32_t r = i / bpr, cb = i - r * bpr;
+    return (r0 + r) * ld + (int64_t)cb * kBlock + 4 * q;
+  };
+  auto load = [&](uint32_t i) { return __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(x + offset(i))); };
+  float S = 0.0f;
+  auto encode = [&](uint32_t i, float4_t v) {
+    const float a = quad_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    float rcp;
+    const uint32_t sig = block_scale(a, S, rcp);
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v.x * rcp, v.y * rcp, 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v.z * rcp, v.w * rcp, 1.0f, 1);
+    const int64_t gi = gbase + i;
+    __builtin_nontemporal_store((uint16_t)w, reinterpret_cast<uint16_t*>(codes + 8 * gi) + q);
+    if (q == 0) scales[gi] = (uint8_t)sig;
+  };
+  // Four blocks per lane in flight; the first four blocks' loads go out
+  // before the partial maxima are reduced.
+  constexpr int U = 4;
+  uint32_t i = wx * BPW + threadIdx.x / 4;
+  float4_t v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (i + u * stride < nblk) v[u] = load(i + u * stride);
+  {
+    const uint32_t np = d + 1 < pdg.ndom ? pdg.full : pdg.last;
+    S = reduce_parts(parts + (int64_t)d * pdg.full, (int)np) / kGlobalMax;
+    if (wx == 0 && threadIdx.x == 0) tscale[d] = S;
+  }
+  while (true) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + u * stride < nblk) encode(i + u * stride, v[u]);
+    i += U * stride;
+    if (i >= nblk) break;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + u * stride < nblk) v[u] = load(i + u * stride);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Column layout (axis 0): x is [rows][ld], 16-element blocks run down the
 // columns and the NVFP4 output is the transpose ([cols][rows/2] codes,
@@ -539,7 +610,17 @@ hipError_t launch_encode_rows(const void* x, int dt, int64_t rows, int64_t cols,
     if (rht) return hipErrorInvalidValue;
     if (dt == 0) NVFP4_ENC_ROWS(0, false, true); else NVFP4_ENC_ROWS(1, false, true);
   } else if (dt == 0) {
-    if (rht) NVFP4_ENC_ROWS(0, true, false); else NVFP4_ENC_ROWS(0, false, false);
+    if (rht) {
+      NVFP4_ENC_ROWS(0, true, false);
+    } else if (ld % 4 == 0 && ((uintptr_t)x & 15) == 0) {  // 16-byte loads
+      // a workgroup covers 64 blocks per sweep and holds four sweeps in flight
+      const DomGrid qg{encode_count(2 * rpd * (cols / kBlock), nd), encode_count(2 * last * (cols / kBlock), nd),
+                       (uint32_t)nd};
+      encode_rows_f32q_kernel<<<total(qg), kThreads, 0, s>>>(static_cast<const float*>(x), rows, cols, ld, rpd, parts,
+                                                              pg, out.codes, out.scales, out.tscale, qg);
+    } else {
+      NVFP4_ENC_ROWS(0, false, false);
+    }
   } else {
     if (rht) NVFP4_ENC_ROWS(1, true, false); else NVFP4_ENC_ROWS(1, false, false);
   }
