@@ -388,8 +388,8 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs, only, settle_ms):
             s = {"x": _dev_bf16(torch, d["x"]), "w": torch.from_numpy(d["w"]).cuda(), "dy": _dev_bf16(torch, d["dy"])}
             s["bufs"] = {"xq": nv.NVFP4Tensor.empty(m, k, 1, "cuda"), "wq": nv.NVFP4Tensor.empty(n, k, 1, "cuda"),
                          "dyq": nv.NVFP4Tensor.empty(m, n, 1, "cuda"), "wtq": nv.NVFP4Tensor.empty(k, n, 1, "cuda"),
-                         "dyt": nv.NVFP4Tensor.empty(n, -(-m // 128) * 128, 1, "cuda"),
-                         "xt": nv.NVFP4Tensor.empty(k, -(-m // 128) * 128, 1, "cuda"),
+                         "dyt": nv.NVFP4Tensor.empty(n, -(-m // 256) * 256, 1, "cuda"),
+                         "xt": nv.NVFP4Tensor.empty(k, -(-m // 256) * 256, 1, "cuda"),
                          "y": torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
                          "dx": torch.empty((m, k), dtype=torch.bfloat16, device="cuda"),
                          "dw": torch.empty((n, k), dtype=torch.float32, device="cuda"),

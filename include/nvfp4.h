@@ -139,7 +139,7 @@ int nvfp4_amax(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
  *             (a multiple of 16): the blocks past rows get zero codes and
  *             zero scales, which decode to 0 and leave a GEMM over the padded
  *             reduction dimension unchanged (nvfp4_gemm runs its fastest path
- *             when K % 64 == 0).
+ *             when K >= 512 and K % 256 == 0).
  * `out` must describe the output shape exactly (for axis 1: rows x cols);
  * out->tscale needs one float per domain.
  */
@@ -217,8 +217,8 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int c_dtyp
  * same W4A4 GEMM: tailorednewshub.com, "Inferencia W4A4 NVFP4").
  * tile_fa x tile_fb is the number of 32x32 MFMA fragments per wavefront
  * along M x N (a workgroup covers 64*tile_fa x 64*tile_fb outputs); the
- * supported shapes are 2x4, 4x2, 3x3, 4x4 and 1x1, used when K >= 128 and
- * K % 64 == 0 (other K always take the bounds-checked 2x4 kernel).  Every
+ * supported shapes are 2x4, 4x2, 3x3, 4x4 and 1x1, used when K >= 512 and
+ * K % 256 == 0 (other K always take the bounds-checked 2x4 kernel).  Every
  * shape accumulates each output element in the same order, so results are
  * bit-identical across shapes.  Unsupported shapes return NVFP4_EINVAL.
  * Intended for tuning and testing.

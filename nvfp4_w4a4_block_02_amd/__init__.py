@@ -422,7 +422,7 @@ def linear_train(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, sign_mask: 
       dw = R(dY^T) R(X^T)^T     (f32)    dY and X quantized along dim 0
 
     Returns (y, dx, dw).  Only sequences C-ABI calls.  Preallocated ``bufs``
-    must give "dyt" / "xt" a K of M rounded up to 128."""
+    must give "dyt" / "xt" a K of M rounded up to 256."""
     b = bufs if bufs is not None else {}
     xq = quantize(x, axis=1, out=b.get("xq"), ws=b.get("ws"), stream=stream)
     # W is quantized along both of its dims with one tensor scale: its amax
@@ -434,9 +434,9 @@ def linear_train(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, sign_mask: 
     wtq = encode(w, wamax, axis=0, out=b.get("wtq"), stream=stream)
     dx = gemm(dyq, wtq, out_dtype=torch.bfloat16, out=b.get("dx"), stream=stream)
     # The weight gradient reduces over M; its operands are zero-padded to a
-    # multiple of 128 along M (exact: zero blocks add nothing) so that the
+    # multiple of 256 along M (exact: zero blocks add nothing) so that the
     # GEMM runs its pipelined path for any token count.
-    mp = -(-x.shape[0] // 128) * 128
+    mp = -(-x.shape[0] // 256) * 256
     dyt = rht16_quantize(dy, sign_mask, axis=0, out=b.get("dyt"), ws=b.get("ws"), stream=stream, k_pad=mp)
     xt = rht16_quantize(x, sign_mask, axis=0, out=b.get("xt"), ws=b.get("ws"), stream=stream, k_pad=mp)
     dw = gemm(dyt, xt, out_dtype=torch.float32, out=b.get("dw"), stream=stream)

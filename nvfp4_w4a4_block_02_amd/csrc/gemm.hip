@@ -24,8 +24,9 @@
 // k = {8s..8s+7} and {64+8s..64+8s+7}.  The MFMA reduction runs over any k as
 // long as A and B use the same assignment, which they do.
 //
-// Main kernel (K >= 128, K % 64 == 0): a 3-stage LDS ring fed by direct
-// global->LDS loads (global_load_lds_dwordx4 / _dword).  Every K-tile is read
+// Main kernel (K >= 512, K % 256 == 0): a 3-stage LDS ring of codes and a
+// 2-slot ring of scales (four K-tiles per slot) fed by direct global->LDS
+// loads (global_load_lds_dwordx4).  Every K-tile is read
 // from memory once per workgroup; its LDS image is laid out in the order the
 // consuming lanes read it (fragment, 16-byte half, lane), so the ds_reads are
 // contiguous and conflict-free.  One barrier per K-tile; the loads of tile
@@ -34,8 +35,8 @@
 // sub-tiles leave through the (then free) LDS ring, transposed into rows, as
 // 16-byte stores; the tensor scales are read during the first tile's wait.
 //
-// Fallback kernel (any K % 16 == 0): the same fragments loaded straight into
-// registers with bounds checks; code bytes past K read as 0.
+// Fallback kernel (any other K % 16 == 0): the same fragments loaded straight
+// into registers with bounds checks; code bytes past K read as 0.
 #include <cmath>
 #include <type_traits>
 
@@ -281,9 +282,8 @@ __device__ __forceinline__ void load_frags_checked(Frags<FA, FB>& fr, const uint
 }
 
 // ---------------------------------------------------------------------------
-// Main kernel: K >= 128, K % 64 == 0.  The K / 128 full tiles go through the
-// LDS pipeline; a remainder of 64 is one bounds-checked tile loaded straight
-// into registers at the end.
+// Main kernel: K >= 512, K % 256 == 0 (code and scale rows 16-byte aligned,
+// an even number of K-tiles); every K-tile goes through the LDS pipeline.
 //
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
 // lgkmcnt[11:8] | vmcnt[5:4] << 14): wait until at most N vector-memory
@@ -311,23 +311,27 @@ __device__ __forceinline__ void step_schedule() {
   }
 }
 
-// Read this wave's fragments of one K-tile from its LDS stage.
+// Read this wave's fragments of one K-tile from its LDS stage (codes) and
+// from the scale ring: `ss` points at the tile's scale bytes inside its
+// 4-tile group (fragment j's 32 rows at 1024 j, 32 bytes per row, 8 per
+// tile), `so` is this lane's row and k-half offset there.
 template <int FA, int FB>
-__device__ __forceinline__ void read_stage(Frags<FA, FB>& fr, const uint8_t* st, int wy, int wx, int l,
-                                           int off_b, int off_sa, int off_sb) {
+__device__ __forceinline__ void read_stage(Frags<FA, FB>& fr, const uint8_t* st, const uint8_t* ss, int so, int wy,
+                                           int wx, int l, int off_b) {
+  constexpr int NFA = 2 * FA;
 #pragma unroll
   for (int f = 0; f < FA; ++f) {
     const int fj = wy * FA + f;
     fr.a[f][0] = *reinterpret_cast<const u32x4_t*>(st + (2 * fj) * 1024 + 16 * l);
     fr.a[f][1] = *reinterpret_cast<const u32x4_t*>(st + (2 * fj + 1) * 1024 + 16 * l);
-    fr.sa[f] = *reinterpret_cast<const uint32_t*>(st + off_sa + fj * 256 + 4 * l);
+    fr.sa[f] = *reinterpret_cast<const uint32_t*>(ss + fj * 1024 + so);
   }
 #pragma unroll
   for (int f = 0; f < FB; ++f) {
     const int fj = wx * FB + f;
     fr.b[f][0] = *reinterpret_cast<const u32x4_t*>(st + off_b + (2 * fj) * 1024 + 16 * l);
     fr.b[f][1] = *reinterpret_cast<const u32x4_t*>(st + off_b + (2 * fj + 1) * 1024 + 16 * l);
-    fr.sb[f] = *reinterpret_cast<const uint32_t*>(st + off_sb + fj * 256 + 4 * l);
+    fr.sb[f] = *reinterpret_cast<const uint32_t*>(ss + (NFA + fj) * 1024 + so);
   }
 }
 
@@ -388,32 +392,46 @@ __device__ __forceinline__ void store_tile_staged(const float16_t (&acc)[FA][FB]
 }
 
 
-// The ring holds three K-tiles.  Every tile body issues exactly L loads
-// (this wave's share of one future tile), so the wait for "tile t+1 landed"
-// is always vmcnt(L), with no branch on the tile index: near the end of K the
-// loads are clamped to the last tile and land in a stage that is never read
-// again.  Tile body t:
-//   1. wait for this wave's loads of tile t+1 and for its LDS reads of tile t
-//      (already in registers), then one barrier: tile t+1 is complete in LDS
-//      and every wave is done reading stage t % 3;
-//   2. issue the LDS reads of tile t+1 (consumed at the end of the body);
+// The code ring holds three K-tiles.  Every tile body issues CPW code loads
+// (this wave's share of one future tile); near the end of K they are clamped
+// to the last tile and land in a stage that is never read again.  Scales
+// travel separately, four K-tiles at a time: one 16-byte load per lane
+// brings 32 bytes of scales for each of a fragment's 32 rows (1 KiB per
+// fragment), into a double-buffered scale ring.  Four-byte scale loads per
+// tile cost ~18% of the attention-projection GEMM (timing variants without
+// them, or with them all on one cache line); this takes four times fewer
+// scale load instructions and half the cache-line accesses.  Scale group g
+// (tiles 4g .. 4g+3, shifted back to end at the last tile when K / 128 is
+// not a multiple of 4) is issued in body 4g - 3 and first read at the start
+// of body 4g - 1, the same two-body lead as the codes.  Tile body t:
+//   1. wait for this wave's loads of tile t+1 (and of scale group (t+1)/4)
+//      and for its LDS reads of tile t (already in registers), then one
+//      barrier: tile t+1 is complete in LDS and every wave is done reading
+//      stage t % 3;
+//   2. issue the LDS reads of tile t+1 (consumed at the end of the body), and
+//      when t % 4 == 1 the loads of scale group (t+3)/4;
 //   3. 8 MFMA steps on tile t, each overlapped with the decode of the next
-//      step and two of the loads of tile t+3 into stage t % 3.
+//      step and the code loads of tile t+3 into stage t % 3.
 template <int FA, int FB, int OUT, int EPI>
 __global__ __launch_bounds__(256) void gemm_lds_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts,
     void* __restrict__ c, int64_t ldc, int M, int N, int K, float* __restrict__ amax_out, int band) {
   constexpr int NFA = 2 * FA, NFB = 2 * FB;                  // fragments per workgroup
-  constexpr int OFF_B = NFA * 2048, OFF_SA = OFF_B + NFB * 2048, OFF_SB = OFF_SA + NFA * 256;
-  constexpr int STAGE = OFF_SB + NFB * 256;
+  constexpr int NFR = NFA + NFB;
+  constexpr int OFF_B = NFA * 2048;
+  constexpr int STAGE = OFF_B + NFB * 2048;                  // codes of one K-tile
+  constexpr int SGROUP = NFR * 1024;                          // scales of one 4-tile group
+  constexpr int SRING = kStages * STAGE;                      // offset of the scale ring
   static_assert((FA + FB) % 2 == 0, "load slots assume FA + FB even");
   constexpr int CPW = FA + FB;        // 16-byte code loads per wave per tile
-  constexpr int SPW = (FA + FB) / 2;  // 4-byte scale loads per wave per tile
-  constexpr int L = CPW + SPW;        // loads per wave per tile
-  constexpr int LPS = (L + 7) / 8;    // loads issued per MFMA step (8 steps per tile)
-  static_assert(3 * L < 64, "three tiles of loads must fit the vmcnt counter");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * STAGE];
+  constexpr int SPW = NFR / 4;        // 16-byte scale loads per wave per 4-tile group
+  static_assert(NFR % 4 == 0, "scale loads are dealt evenly over the 4 waves");
+  constexpr int LPS = (CPW + 7) / 8;  // code loads issued per MFMA step (8 steps per tile)
+  static_assert(3 * CPW + SPW < 64, "three tiles of loads must fit the vmcnt counter");
+  constexpr bool kStaged = OUT == 1 && (FB == 2 || FB == 4);  // bf16 epilogue through LDS
+  constexpr int SMEM = kStaged && 4 * kOutRegion > SRING + 2 * SGROUP ? 4 * kOutRegion : SRING + 2 * SGROUP;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
 
   const int l = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS destinations in SGPRs
@@ -425,17 +443,19 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
   const int mwg = tm * 64 * FA, nwg = tn * 64 * FB;
   const int64_t cpitch = K / 2, spitch = K / 16;
 
-  // Load slots: code loads (2 per fragment) and scale loads (1 per fragment)
-  // dealt round-robin over the 4 waves.  Lane l of a code load fetches the
-  // 16-byte half q of row (32 f + l % 32), k-half l / 32; rows past M / N are
+  // Load slots: code loads (2 per fragment per tile) and scale loads (1 per
+  // fragment per 4-tile group) dealt round-robin over the 4 waves.  Lane l of
+  // a code load fetches the 16-byte half q of row (32 f + l % 32), k-half
+  // l / 32; lane l of a scale load fetches bytes 16 (l % 2) .. 16 (l % 2) + 15
+  // of the group's 32 scale bytes of row (32 f + l / 2); rows past M / N are
   // clamped (computed, never stored).  The address of a load is a uniform
   // base (the operand, advanced per K-tile) plus a 32-bit lane offset (the
   // host takes this path only for operands below 2^31 bytes), so it goes out
   // with a scalar base and the LDS destination is uniform too: no per-load
   // 64-bit vector arithmetic.
-  const uint8_t* base[L];
-  uint32_t off[L];
-  int dst[L];
+  const uint8_t* base[CPW + SPW];
+  uint32_t off[CPW + SPW];
+  int dst[CPW + SPW];
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
     const int i = wave + 4 * j;  // 0 .. 2 (NFA + NFB) - 1
@@ -448,23 +468,40 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
   }
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
-    const int i = wave + 4 * j;  // 0 .. NFA + NFB - 1
+    const int i = wave + 4 * j;  // 0 .. NFR - 1
     const bool isA = i < NFA;
     const int f = isA ? i : i - NFA;
-    const int row = isA ? min(mwg + 32 * f + li, M - 1) : min(nwg + 32 * f + li, N - 1);
+    const int row = isA ? min(mwg + 32 * f + (l >> 1), M - 1) : min(nwg + 32 * f + (l >> 1), N - 1);
     base[CPW + j] = isA ? as : bs;
-    off[CPW + j] = (uint32_t)row * (uint32_t)spitch + 4 * hh;
-    dst[CPW + j] = (isA ? OFF_SA : OFF_SB) + f * 256;
+    off[CPW + j] = (uint32_t)row * (uint32_t)spitch + 16 * (l & 1);
+    dst[CPW + j] = i * 1024;
   }
-  // Load j of tile `tile` into the stage at `st`.
+  const int nt = K / kKT;       // >= 4 on this path
+  const int ng = (nt + 3) / 4;  // scale groups
+  // First tile of scale group g (the last group is shifted back so that its
+  // 32 bytes per row stay inside the row).
+  auto gstart = [&](int g) { return min(4 * g, nt - 4); };
+  // Code load j of tile `tile` into the stage at `st`.
   auto load = [&](int j, int tile, uint8_t* st) {
     if (j < CPW)
       __builtin_amdgcn_global_load_lds((gvoid_t*)(base[j] + (int64_t)tile * (kKT / 2) + off[j]), (lvoid_t*)(st + dst[j]),
                                        16, 0, 0);
-    else if (j < L)
-      __builtin_amdgcn_global_load_lds((gvoid_t*)(base[j] + (int64_t)tile * (kKT / 16) + off[j]), (lvoid_t*)(st + dst[j]),
-                                       4, 0, 0);
   };
+  // The scale loads of group g (clamped to the last group) into ring slot g % 2.
+  auto load_scales = [&](int g) {
+    const int64_t b0 = (int64_t)gstart(min(g, ng - 1)) * (kKT / 16);
+    uint8_t* const sl = smem + SRING + (g & 1) * SGROUP;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+      __builtin_amdgcn_global_load_lds((gvoid_t*)(base[CPW + j] + b0 + off[CPW + j]), (lvoid_t*)(sl + dst[CPW + j]), 16,
+                                       0, 0);
+  };
+  // Scale bytes of tile u in the ring, and this lane's offset within a fragment.
+  auto sbase = [&](int u) -> const uint8_t* {
+    const int g = u >> 2;
+    return smem + SRING + (g & 1) * SGROUP + 8 * (u - gstart(g));
+  };
+  const int so = 32 * li + 4 * hh;
 
   const int wy = wave >> 1, wx = wave & 1;
   float16_t acc[FA][FB];
@@ -475,29 +512,35 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nt = K / kKT;
+  load_scales(0);
 #pragma unroll
   for (int t = 0; t < kStages; ++t) {
 #pragma unroll
-    for (int j = 0; j < L; ++j) load(j, min(t, nt - 1), smem + t * STAGE);
+    for (int j = 0; j < CPW; ++j) load(j, min(t, nt - 1), smem + t * STAGE);
   }
   // The tensor scales, read now so that their latency hides under the wait
   // for the first tile instead of delaying the epilogue.
   float sab = ats[0] * bts[0];
   asm volatile("" : "+v"(sab));
-  wait_vmcnt<2 * L>();  // tile 0 landed (this wave's part)
+  wait_vmcnt<2 * CPW>();  // scale group 0 and tile 0 landed (this wave's part)
   __builtin_amdgcn_s_barrier();
 
   Frags<FA, FB> F0, F1;
   half8_t A0[FA], B0[FB], A1[FA], B1[FB];
-  read_stage(F0, smem, wy, wx, l, OFF_B, OFF_SA, OFF_SB);
+  read_stage(F0, smem, sbase(0), so, wy, wx, l, OFF_B);
   decode_step(F0, 0, A0, B0);
 
   auto body = [&](int t, const Frags<FA, FB>& cur, Frags<FA, FB>& nxt) {
-    wait_vmcnt<L>();
+    // Outstanding loads allowed: those body t-1 issued (codes of tile t+2,
+    // plus a scale group when t - 1 = 1 mod 4).
+    if ((t & 3) == 2) wait_vmcnt<CPW + SPW>();
+    else wait_vmcnt<CPW>();
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
-    read_stage(nxt, smem + ((t + 1) % kStages) * STAGE, wy, wx, l, OFF_B, OFF_SA, OFF_SB);
+    // (in the last body the next tile does not exist: its decode is never
+    // used, and its scale bytes are read at the last tile's, in bounds)
+    read_stage(nxt, smem + ((t + 1) % kStages) * STAGE, sbase(min(t + 1, nt - 1)), so, wy, wx, l, OFF_B);
+    if ((t & 3) == 1) load_scales((t + 3) >> 2);
     uint8_t* const ist = smem + (t % kStages) * STAGE;
     const int tl = min(t + kStages, nt - 1);
 #pragma unroll
@@ -525,35 +568,13 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
   if (t < nt) body(t, F0, F1);
   wait_vmcnt<0>();  // no load into LDS may be in flight when the workgroup ends
 
-  if (K % kKT != 0) {
-    const uint8_t* pa[FA];
-    const uint8_t* psa[FA];
-    const uint8_t* pb[FB];
-    const uint8_t* psb[FB];
-#pragma unroll
-    for (int f = 0; f < FA; ++f) {
-      const int row = min(mwg + wy * 32 * FA + 32 * f + li, M - 1);
-      pa[f] = ac + (int64_t)row * cpitch + 32 * hh;
-      psa[f] = as + (int64_t)row * spitch + 4 * hh;
-    }
-#pragma unroll
-    for (int f = 0; f < FB; ++f) {
-      const int col = min(nwg + wx * 32 * FB + 32 * f + li, N - 1);
-      pb[f] = bc + (int64_t)col * cpitch + 32 * hh;
-      psb[f] = bs + (int64_t)col * spitch + 4 * hh;
-    }
-    Frags<FA, FB> fr;
-    load_frags_checked(fr, pa, psa, pb, psb, nt * kKT, hh, K);
-    compute_tile(fr, acc);
-  }
-
   const int m0 = mwg + wy * 32 * FA, n0 = nwg + wx * 32 * FB;
-  if constexpr (OUT == 1 && (FB == 2 || FB == 4)) {
+  if constexpr (kStaged) {
     // Every wave has finished with the LDS ring (its loads landed, its reads
     // done) before any wave overwrites it with output.
     __syncthreads();
     const bool whole = m0 + 32 * FA <= M && n0 + 32 * FB <= N && ldc % 8 == 0 && ((uintptr_t)c & 15) == 0;
-    static_assert(4 * kOutRegion <= kStages * STAGE, "the staging regions reuse the LDS ring");
+    static_assert(4 * kOutRegion <= SMEM, "the staging regions reuse the LDS rings");
     if (whole) {
       store_tile_staged<FA, FB, EPI>(acc, sab, m0, n0, l, li, hh, smem + wave * kOutRegion, static_cast<uint16_t*>(c),
                                      ldc, amax_out);
@@ -564,7 +585,7 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Fallback kernel: K < 128, K % 64 != 0 or misaligned operands (fragments
+// Fallback kernel: K < 512, K % 256 != 0 or misaligned operands (fragments
 // straight from global memory, bounds-checked along K).
 template <int FA, int FB, int OUT, int EPI>
 __global__ __launch_bounds__(256) void gemm_checked_kernel(
@@ -689,11 +710,11 @@ hipError_t launch_gemm(QOut a, QOut b, int64_t m, int64_t n, int64_t k, void* c,
     if (e != hipSuccess) return e;
   }
   const Args g{a, b, (int)m, (int)n, (int)k, c, ldc, amax_out};
-  // LDS path: K >= 128 and K % 64 == 0, so every code row starts 16-byte
-  // aligned and every scale row 4-byte aligned (the direct-to-LDS loads need
-  // both); a remainder of 64 goes through the checked tail tile.
-  const bool lds_path = (k >= kKT) && (k % 64 == 0) && ((uintptr_t)a.codes % 16 == 0) && ((uintptr_t)b.codes % 16 == 0) &&
-                        ((uintptr_t)a.scales % 4 == 0) && ((uintptr_t)b.scales % 4 == 0) &&
+  // LDS path: K >= 512 (one scale group of four K-tiles) and K % 256 == 0,
+  // so every code and scale row, and every scale group's first byte, is
+  // 16-byte aligned as the direct-to-LDS 16-byte loads need.
+  const bool lds_path = (k >= 4 * kKT) && (k % 256 == 0) && ((uintptr_t)a.codes % 16 == 0) &&
+                        ((uintptr_t)b.codes % 16 == 0) && ((uintptr_t)a.scales % 16 == 0) && ((uintptr_t)b.scales % 16 == 0) &&
                         m * (k / 2) < ((int64_t)1 << 31) && n * (k / 2) < ((int64_t)1 << 31);  // 32-bit load offsets
   if (lds_path) {
     auto run = [&](int fa, int fb, const Args& ar) {

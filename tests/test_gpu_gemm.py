@@ -2,7 +2,8 @@
 |gpu - C| <= 1e-5 * sum_k |P_A P_B| per element (plus half a bf16 ulp for bf16
 outputs).  Operand codes are first checked bit-exact against the oracle's own
 quantization, so both sides multiply the same NVFP4 numbers.  Covers ragged
-M/N/K tails (the K-checked path and the K % 128 fast path), fp32/bf16
+M/N/K tails (the K-checked path and the pipelined path for K >= 512,
+K % 256 == 0, with K / 128 both a multiple of 4 and not), fp32/bf16
 outputs, the GELU epilogue with its amax reduction, and the workload shapes
 (tiny linear, attention projection, FFN pair stage by stage, weight-gradient
 GEMM after the RHT, the training triple) at full size, where every output row
@@ -94,13 +95,13 @@ def test_tile_shapes_are_bit_identical(nv, m, n, k):
 
 
 def test_split_last_tile_row(nv):
-    """2144 x 8192: the automatic choice (128 x 256 tiles) would leave a last
+    """2144 x 8192 (K = 512): the automatic choice (128 x 256 tiles) would leave a last
     tile row of 96 rows that costs a third round of workgroups, so the 2048
     full tile rows and the 96 remaining rows run as two launches (the second
     with 64 x 64 tiles).  The result is bit-identical to one launch with
     pinned tiles, float32 and the bf16 GELU epilogue with its amax alike, and
     the rows on both sides of the seam match the float64 oracle."""
-    m, n, k = 2144, 8192, 256
+    m, n, k = 2144, 8192, 512
     log(f"gemm split of the last tile row {m}x{n}x{k}")
     rng = np.random.default_rng(2144)
     ga, gb, oa, ob = _operands(nv, rng, m, n, k)
@@ -368,12 +369,12 @@ def test_train_linear_triple_full(nv):
     input gradient and weight gradient.  The six operands linear_train
     itself built (passed in as buffers) are compared with the oracle's
     quantizers byte for byte (the two RHT16 operands with their zero padding
-    from M = 2640 to 2688), and every row of the three GEMMs is within the
+    from M = 2640 to 2816), and every row of the three GEMMs is within the
     parity bound."""
     d = workloads.train_linear()
     log("workload 6: training triple of a 2640x3072x3072 linear layer")
     x, w, dy = dev_bf16(d["x"]), dev_f32(d["w"]), dev_bf16(d["dy"])
-    m, k, n, mp = 2640, 3072, 3072, 2688
+    m, k, n, mp = 2640, 3072, 3072, 2816
     bufs = {"xq": nv.NVFP4Tensor.empty(m, k), "wq": nv.NVFP4Tensor.empty(n, k), "dyq": nv.NVFP4Tensor.empty(m, n),
             "wtq": nv.NVFP4Tensor.empty(k, n), "dyt": nv.NVFP4Tensor.empty(n, mp), "xt": nv.NVFP4Tensor.empty(k, mp)}
     y, dx, dw = nv.linear_train(x, w, dy, d["mask"], bufs=bufs)
