@@ -290,12 +290,16 @@ int nvfp4_kv_dequant(const nvfp4_tensor *in, int64_t frames, int64_t tokens, int
  * accumulation (decoded elements are exact in fp16; q enters with a per-row
  * power-of-two scale); probabilities are rounded to fp16.  Results agree with
  * an exact computation to about 2^-10 of sum_j p_j |V_j| / sum_j p_j per
- * element (plus the bf16 rounding of the output).
+ * element (plus the bf16 rounding of the output), except where the output is
+ * carried by keys weighted below about 2^-24 of the largest (fp16's
+ * subnormal range): there the error can reach 2^-25 sum_j |V_j| / L over
+ * those keys, L = sum_j p_j / max_j p_j.
  *
  * Frame blocks may hold any number of keys (frame_block * tokens); a
  * frame_block >= frames means one block over the whole window, as in
- * nvfp4_kv_dequant.  Limits: head_dim must be 128 (else NVFP4_EUNSUPPORTED);
- * 1 <= q_frames <= frames.  A non-finite value anywhere in the keys a
+ * nvfp4_kv_dequant.  Limits: head_dim must be 64 or 128 (else
+ * NVFP4_EUNSUPPORTED); 1 <= q_frames <= frames; the cache's code bytes
+ * (frames * tokens * heads * head_dim / 2) below 2^31.  A non-finite value anywhere in the keys a
  * workgroup of 128 queries scans can propagate to its outputs.  No workspace.
  */
 int nvfp4_kv_attention(const void *q, int64_t q_frames, const nvfp4_tensor *k, const nvfp4_tensor *v,

@@ -301,21 +301,21 @@ int nvfp4_kv_attention(const void* q, int64_t q_frames, const nvfp4_tensor* k, c
     return NVFP4_EINVAL;
   const int64_t rows = mul_sat(mul_sat(frames, tokens), heads);
   // 32-bit offsets: code bytes of the cache and the workgroup count
-  if (mul_sat(rows, 64) >= ((int64_t)1 << 31)) return NVFP4_EUNSUPPORTED;
+  if (mul_sat(rows, head_dim / 2) >= ((int64_t)1 << 31)) return NVFP4_EUNSUPPORTED;
   if (!tensor_ok(k) || !tensor_ok(v) || k->rows != rows || v->rows != rows || k->k != head_dim ||
       v->k != head_dim)
     return NVFP4_EINVAL;
   const int64_t nq = q_frames * tokens;  // <= rows
   if (nq == 0 || heads == 0) return NVFP4_OK;
-  if (head_dim != 128) return NVFP4_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return NVFP4_EUNSUPPORTED;
   if (((nq + 127) / 128) * heads >= ((int64_t)1 << 31)) return NVFP4_EUNSUPPORTED;
   // One frame block covers the whole window when frame_block >= frames (as
   // in nvfp4_kv_dequant); the kernel then sees at most frames * tokens keys
   // per block.
   const int64_t fb = frame_block < frames ? frame_block : frames;
   return from_hip(nvfp4::launch_kv_attention(static_cast<const uint16_t*>(q), qout(k), qout(v), out,
-                                             out_dtype == NVFP4_F32, nq, tokens, heads, frames, q_frames,
-                                             fb, (hipStream_t)stream));
+                                             out_dtype == NVFP4_F32, nq, tokens, heads, head_dim, frames,
+                                             q_frames, fb, (hipStream_t)stream));
 }
 
 int nvfp4_dequantize(const nvfp4_tensor* in, int64_t rows_per_domain, void* out, int dtype, void* stream) {

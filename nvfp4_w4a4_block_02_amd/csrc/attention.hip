@@ -9,10 +9,11 @@
 // attention loop, so the cache is read once per workgroup at 4.5 bits per
 // element and the bf16 window is never written.
 //
-//   O[q, h, :] = sum_j softmax_j(Q[q,h,:] . K[j,h,:] / sqrt(128)) V[j,h,:]
+//   O[q, h, :] = sum_j softmax_j(Q[q,h,:] . K[j,h,:] / sqrt(D)) V[j,h,:]
 //   over the keys j of frames 0 .. frame(q)   (frame-level causal mask)
 //
-// with K, V = e2m1(code) * s_b * S exactly as the codec defines them.
+// with K, V = e2m1(code) * s_b * S exactly as the codec defines them, for a
+// head dimension D of 64 or 128 (one kernel instance each).
 //
 // Arithmetic.  A decoded element e2m1 * s_b has at most 6 significant bits and
 // lies in [2^-10, 2688], so it is exact in fp16; both products run on
@@ -21,19 +22,21 @@
 //     query row that puts the row maximum in [2^14, 2^15): every bf16 value
 //     within 2^-29 of the row maximum converts exactly, and smaller ones move
 //     the dot product by less than float32 accumulation does.  The row scale,
-//     the K tensor scale of the tile's frame block and log2(e)/sqrt(128) are
+//     the K tensor scale of the tile's frame block and log2(e)/sqrt(D) are
 //     one float32 factor per lane applied to the accumulator.
 //   * Softmax in base 2 with a running maximum per query.  The maximum is only
 //     moved when the new tile exceeds it by more than 8 (a factor 256), so the
 //     accumulator is rescaled rarely; probabilities stay <= 256 and go to fp16
-//     (11 significant bits).
+//     (11 significant bits above 2^-14; below, fp16 subnormals round to a
+//     multiple of 2^-24, which only matters when the keys weighted below
+//     about 2^-24 of the largest carry the output).
 //   * O^T = V^T P^T.  The accumulator is kept in units of one V tensor scale and
 //     rescaled by the ratio when a key block with another frame-block scale
 //     arrives (once per frame-block boundary).
 //
 // Work split.  A workgroup of 4 wavefronts owns 128 queries of one head;
 // wavefront w takes queries 32w .. 32w+31 (one 32-query MFMA column) over all
-// keys, so each wavefront runs 16 + 16 MFMAs per 64-key tile.  Two workgroups
+// keys, so each wavefront runs D/8 + D/8 MFMAs per 64-key tile.  Two workgroups
 // share a CU, so the two wavefronts on a SIMD come from different workgroups
 // and their MFMA and VALU work interleaves.  Lanes own queries: in the
 // transposed products each lane holds one query column, so the row maximum,
@@ -51,6 +54,7 @@
 // block end are masked (they belong to the next block's first tile); when it
 // is (e.g. 8 frames of 880 tokens), tile t simply starts at key 64 t.
 #include <cmath>
+#include <type_traits>
 
 #include "device.h"
 #include "internal.h"
@@ -58,25 +62,41 @@
 namespace nvfp4 {
 namespace {
 
-constexpr int kD = 128;                  // head_dim
 constexpr int kQT = 128;                 // queries per workgroup
 constexpr int kKT = 64;                  // keys per tile
-constexpr int kKRow = 2 * kD + 16;       // bytes per decoded K row (fp16, padded)
 constexpr int kVRow = 2 * kKT + 16;      // bytes per decoded V^T row (fp16, padded)
-constexpr int kKBuf = kKT * kKRow;       // 17408
-constexpr int kVBuf = kD * kVRow;        // 18432
-constexpr int kBuf = kKBuf + kVBuf;
-constexpr int kLds = 2 * kBuf;           // 71680
 constexpr float kMInit = -1.0e30f;       // finite: exp2(kMInit - m) = 0, exp2(0) = 1
 constexpr float kLazy = 8.0f;            // rescale threshold (log2 units)
-constexpr float kLog2eRsqrtD = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
+
+// Sizes that follow the head dimension D (64 or 128).  Lane duties: in the
+// K decode lane (key, wave) owns d in [D/4 * wave, +D/4) (D/8 code bytes);
+// in the V decode lane (kg, dc) owns 4 keys x D/16 elements (D/32 code bytes
+// per key).
+template <int D>
+struct Dim {
+  static_assert(D == 64 || D == 128, "head dimension 64 or 128");
+  static constexpr int kKRow = 2 * D + 16;     // bytes per decoded K row (fp16, padded)
+  static constexpr int kKBuf = kKT * kKRow;    // 17408 at D = 128
+  static constexpr int kVBuf = D * kVRow;      // 18432 at D = 128
+  static constexpr int kBuf = kKBuf + kVBuf;
+  static constexpr int kLds = 2 * kBuf;        // 71680 at D = 128
+  static constexpr int kSteps = D / 16;        // k-steps of the score MFMA
+  static constexpr int kDB = D / 32;           // 32-wide d blocks of the output
+  static constexpr int kRow = D / 2;           // code bytes per cache row
+  static constexpr int kKW = D / 32;           // 32-bit code words per lane of a K tile
+  using KWords = std::conditional_t<D == 128, u32x4_t, u32x2_t>;
+  static constexpr int kVB = D / 32;           // code bytes per key per lane of a V tile
+  // log2(e) / sqrt(D)
+  static constexpr float kLog2eRsqrtD = 1.4426950408889634f * (D == 64 ? 0.125f : 0.08838834764831845f);
+};
 
 // Raw codes of one tile held by a lane between its load and its decode.
+template <int D>
 struct Raw {
-  u32x4_t kc;       // 32 K codes: key (lane & 63), d in [32 * wave, +32)
-  uint32_t ks;      // their two E4M3 block scales (low 16 bits)
-  uint32_t vc[4];   // 8 V codes (d in [8 * dc, +8)) of keys 4 * kg + r
-  uint32_t vs[4];   // the V block scale of each of those keys
+  typename Dim<D>::KWords kc;   // D/4 K codes: key (lane & 63), d in [D/4 * wave, +D/4)
+  uint32_t ks;                  // their E4M3 block scales (low D/64 bytes)
+  uint32_t vc[4];               // D/16 V codes (d in [D/16 * dc, +D/16)) of keys 4 * kg + r
+  uint32_t vs[4];               // the V block scale of each of those keys
 };
 
 struct Geo {
@@ -86,42 +106,62 @@ struct Geo {
   const uint8_t* vs;
   int heads, h, nkeys;
   // byte offsets of this lane's code loads from the first code row of a tile
-  // (scale offsets are these >> 3: 64 code bytes and 8 scale bytes per row)
+  // (scale offsets are these >> 3: a row has D/2 code bytes and D/16 scale
+  // bytes, 8 code bytes per scale byte)
   uint32_t okc, ovc[4];
 };
 
+template <int D>
 __device__ __forceinline__ void init_geo(Geo& g, int tid) {
-  const uint32_t rb = (uint32_t)g.heads * 64u;       // code bytes between consecutive keys
-  g.okc = (uint32_t)(tid & 63) * rb + 16u * (uint32_t)(tid >> 6);
+  const uint32_t rb = (uint32_t)g.heads * Dim<D>::kRow;   // code bytes between consecutive keys
+  g.okc = (uint32_t)(tid & 63) * rb + (uint32_t)(4 * Dim<D>::kKW) * (uint32_t)(tid >> 6);
   const int kg = tid & 15, dc = tid >> 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) g.ovc[i] = (uint32_t)(4 * kg + i) * rb + 4u * (uint32_t)dc;
+  for (int i = 0; i < 4; ++i) g.ovc[i] = (uint32_t)(4 * kg + i) * rb + (uint32_t)Dim<D>::kVB * (uint32_t)dc;
 }
 
-// Raw codes of K tile key0 (32 code bytes + 2 scale bytes per lane).
-__device__ __forceinline__ void load_raw_k(const Geo& g, int key0, int tid, Raw& r) {
+// The lane's V code bytes of one key at p (D/32 bytes).
+template <int D>
+__device__ __forceinline__ uint32_t load_vbytes(const uint8_t* p) {
+  if constexpr (D == 128) return *reinterpret_cast<const uint32_t*>(p);
+  else return *reinterpret_cast<const uint16_t*>(p);
+}
+// The K block scales of one lane (D/64 bytes) at p.
+template <int D>
+__device__ __forceinline__ uint32_t load_kscales(const uint8_t* p) {
+  if constexpr (D == 128) return *reinterpret_cast<const uint16_t*>(p);
+  else return *p;
+}
+
+// Raw codes of K tile key0 (D/8 code bytes + D/64 scale bytes per lane).
+template <int D>
+__device__ __forceinline__ void load_raw_k(const Geo& g, int key0, int tid, Raw<D>& r) {
+  constexpr uint32_t kRow = Dim<D>::kRow;
   if (key0 + kKT <= g.nkeys) {
     const uint32_t row0 = (uint32_t)key0 * (uint32_t)g.heads + (uint32_t)g.h;
-    r.kc = *reinterpret_cast<const u32x4_t*>(g.kc + (size_t)row0 * 64u + g.okc);
-    r.ks = *reinterpret_cast<const uint16_t*>(g.ks + (size_t)row0 * 8u + (g.okc >> 3));
+    r.kc = *reinterpret_cast<const typename Dim<D>::KWords*>(g.kc + (size_t)row0 * kRow + g.okc);
+    r.ks = load_kscales<D>(g.ks + (size_t)row0 * (kRow / 8) + (g.okc >> 3));
     return;
   }
   // last, partial tile: rows past the end re-read the last key (masked)
   const int key = min(key0 + (tid & 63), g.nkeys - 1);
   const uint32_t row = (uint32_t)key * (uint32_t)g.heads + (uint32_t)g.h;
-  r.kc = *reinterpret_cast<const u32x4_t*>(g.kc + row * 64u + 16u * (uint32_t)(tid >> 6));
-  r.ks = *reinterpret_cast<const uint16_t*>(g.ks + row * 8u + 2u * (uint32_t)(tid >> 6));
+  const uint32_t wave = (uint32_t)(tid >> 6);
+  r.kc = *reinterpret_cast<const typename Dim<D>::KWords*>(g.kc + row * kRow + (D / 8) * wave);
+  r.ks = load_kscales<D>(g.ks + row * (kRow / 8) + (D / 64) * wave);
 }
 
-// Raw codes of V tile key0 (4 keys x 8 elements per lane).
-__device__ __forceinline__ void load_raw_v(const Geo& g, int key0, int tid, Raw& r) {
+// Raw codes of V tile key0 (4 keys x D/16 elements per lane).
+template <int D>
+__device__ __forceinline__ void load_raw_v(const Geo& g, int key0, int tid, Raw<D>& r) {
+  constexpr uint32_t kRow = Dim<D>::kRow;
   if (key0 + kKT <= g.nkeys) {
     const uint32_t row0 = (uint32_t)key0 * (uint32_t)g.heads + (uint32_t)g.h;
-    const uint8_t* vcb = g.vc + (size_t)row0 * 64u;
-    const uint8_t* vsb = g.vs + (size_t)row0 * 8u;
+    const uint8_t* vcb = g.vc + (size_t)row0 * kRow;
+    const uint8_t* vsb = g.vs + (size_t)row0 * (kRow / 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      r.vc[i] = *reinterpret_cast<const uint32_t*>(vcb + g.ovc[i]);
+      r.vc[i] = load_vbytes<D>(vcb + g.ovc[i]);
       r.vs[i] = vsb[g.ovc[i] >> 3];
     }
     return;
@@ -131,8 +171,8 @@ __device__ __forceinline__ void load_raw_v(const Geo& g, int key0, int tid, Raw&
   for (int i = 0; i < 4; ++i) {
     const int key = min(key0 + 4 * kg + i, g.nkeys - 1);
     const uint32_t row = (uint32_t)key * (uint32_t)g.heads + (uint32_t)g.h;
-    r.vc[i] = *reinterpret_cast<const uint32_t*>(g.vc + row * 64u + 4u * dc);
-    r.vs[i] = g.vs[row * 8u + (dc >> 1)];
+    r.vc[i] = load_vbytes<D>(g.vc + row * kRow + (uint32_t)Dim<D>::kVB * dc);
+    r.vs[i] = g.vs[row * (kRow / 8) + (dc >> (D == 128 ? 1 : 2))];   // 16 elements per scale
   }
 }
 
@@ -147,16 +187,17 @@ __device__ __forceinline__ half8_t decode8(uint32_t codes, half2_t sig2) {
   return r;
 }
 
-// K tile, row-major: K_lds[key][d], fp16, row pitch kKRow.
-__device__ __forceinline__ void decode_k(const Raw& r, uint8_t* buf, int tid) {
+// K tile, row-major: K_lds[key][d], fp16, row pitch kKRow.  Code word w
+// (8 elements) takes block scale w / 2.
+template <int D>
+__device__ __forceinline__ void decode_k(const Raw<D>& r, uint8_t* buf, int tid) {
   const int wave = tid >> 6, key = tid & 63;
   const half2_t s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.ks, 1.0f, false);
   const half2_t s0 = {s.x, s.x}, s1 = {s.y, s.y};
-  uint8_t* dst = buf + key * kKRow + 64 * wave;
-  *reinterpret_cast<half8_t*>(dst + 0) = decode8(r.kc[0], s0);
-  *reinterpret_cast<half8_t*>(dst + 16) = decode8(r.kc[1], s0);
-  *reinterpret_cast<half8_t*>(dst + 32) = decode8(r.kc[2], s1);
-  *reinterpret_cast<half8_t*>(dst + 48) = decode8(r.kc[3], s1);
+  uint8_t* dst = buf + key * Dim<D>::kKRow + Dim<D>::kRow * wave;
+#pragma unroll
+  for (int w = 0; w < Dim<D>::kKW; ++w)
+    *reinterpret_cast<half8_t*>(dst + 16 * w) = decode8(r.kc[w], w < 2 ? s0 : s1);
 }
 
 // Code byte B of the interleaved key pairs: d = 2B (lo) and d = 2B + 1 (hi)
@@ -175,15 +216,17 @@ __device__ __forceinline__ void v_byte(uint32_t lo01, uint32_t hi01, uint32_t lo
   *reinterpret_cast<u32x2_t*>(dst + (2 * B + 1) * kVRow) = wo;
 }
 
-// V tile, transposed: Vt_lds[d][key'], fp16, row pitch kVRow.  key' permutes
+// V tile, transposed: Vt_lds[d][key'], fp16, row pitch kVRow, after the K
+// tile in the buffer.  key' permutes
 // the key offset o (0..63) by swapping its bits 2 and 3: the second MFMA's
 // k-step u of key block b then reads, in lane half hf, the 8 keys
 // 32b + 16u + {0,1,2,3,8,9,10,11} + 4hf contiguously — exactly the keys whose
 // probabilities that lane holds from the first MFMA's output layout.
-// Each lane decodes 4 consecutive keys x 8 d and writes one 8-byte group of 4
-// keys per d; the two nibble streams of a key pair are interleaved first so
+// Each lane decodes 4 consecutive keys x D/16 d and writes one 8-byte group of
+// 4 keys per d; the two nibble streams of a key pair are interleaved first so
 // that one conversion yields the pair (key0, key1) at the same d.
-__device__ __forceinline__ void decode_v(const Raw& r, uint8_t* buf, int tid) {
+template <int D>
+__device__ __forceinline__ void decode_v(const Raw<D>& r, uint8_t* buf, int tid) {
   const int kg = tid & 15, dc = tid >> 4;
   const int kgp = (kg & ~3) | ((kg & 1) << 1) | ((kg >> 1) & 1);
   const uint32_t m = 0x0F0F0F0Fu;
@@ -193,16 +236,19 @@ __device__ __forceinline__ void decode_v(const Raw& r, uint8_t* buf, int tid) {
   const uint32_t hi23 = ((r.vc[2] >> 4) & m) | (r.vc[3] & ~m);
   const half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.vs[0] | (r.vs[1] << 8), 1.0f, false);
   const half2_t s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.vs[2] | (r.vs[3] << 8), 1.0f, false);
-  uint8_t* dst = buf + kKBuf + (8 * dc) * kVRow + 8 * kgp;
+  uint8_t* dst = buf + Dim<D>::kKBuf + (2 * Dim<D>::kVB * dc) * kVRow + 8 * kgp;
   v_byte<0>(lo01, hi01, lo23, hi23, s01, s23, dst);
   v_byte<1>(lo01, hi01, lo23, hi23, s01, s23, dst);
-  v_byte<2>(lo01, hi01, lo23, hi23, s01, s23, dst);
-  v_byte<3>(lo01, hi01, lo23, hi23, s01, s23, dst);
+  if constexpr (Dim<D>::kVB == 4) {
+    v_byte<2>(lo01, hi01, lo23, hi23, s01, s23, dst);
+    v_byte<3>(lo01, hi01, lo23, hi23, s01, s23, dst);
+  }
 }
 
 // Softmax and output state of one wavefront (32 queries, one per lane column).
+template <int D>
 struct State {
-  float16_t acc[4];   // O^T for d block db (32 d), in units of svref
+  float16_t acc[Dim<D>::kDB];   // O^T for d block db (32 d), in units of svref
   float m;            // running maximum of the scaled scores (base 2), equal in lanes c and c + 32
   float l;            // partial row sum over this lane's keys
   float svref;        // V tensor scale the accumulator is expressed in (0: none yet)
@@ -210,13 +256,15 @@ struct State {
 
 // S^T = K Q^T for one 64-key tile (two 32-key blocks) of the wavefront's 32
 // queries; kbuf holds the decoded K tile.
-__device__ __forceinline__ void qk_tile(const uint8_t* kbuf, int c, int hf, const half8_t (&qf)[8],
+template <int D>
+__device__ __forceinline__ void qk_tile(const uint8_t* kbuf, int c, int hf, const half8_t (&qf)[Dim<D>::kSteps],
                                         float16_t (&sacc)[2]) {
+  constexpr int kKRow = Dim<D>::kKRow;
 #pragma unroll
   for (int i = 0; i < 16; ++i) { sacc[0][i] = 0.0f; sacc[1][i] = 0.0f; }
   const uint8_t* ka = kbuf + c * kKRow + 16 * hf;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
+  for (int s = 0; s < Dim<D>::kSteps; ++s) {
     const half8_t a0 = *reinterpret_cast<const half8_t*>(ka + 32 * s);
     const half8_t a1 = *reinterpret_cast<const half8_t*>(ka + 32 * kKRow + 32 * s);
     sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qf[s], sacc[0], 0, 0, 0);
@@ -228,9 +276,9 @@ __device__ __forceinline__ void qk_tile(const uint8_t* kbuf, int c, int hf, cons
 // its K tensor scale).  Produces the fp16 probabilities and returns the factor
 // the accumulator must be multiplied by before they are added (1 unless the
 // running maximum moved).  MASK: apply the per-query key limit.
-template <bool MASK>
+template <bool MASK, int D>
 __device__ __forceinline__ float softmax_tile(float16_t (&sacc)[2], int key0, int hf, float cq, int lim, float sk,
-                                              State& st, half8_t (&pb)[2][2]) {
+                                              State<D>& st, half8_t (&pb)[2][2]) {
   // Scaled scores s = raw * cs, rounded to float32 first and the maximum
   // taken over those same values, so the maximum's exponent is exactly 0 at
   // any magnitude (an fma against a rounded maximum would leave a residual
@@ -278,22 +326,24 @@ __device__ __forceinline__ float softmax_tile(float16_t (&sacc)[2], int key0, in
   return alpha;
 }
 
-__device__ __forceinline__ void rescale(State& st, float f) {
+template <int D>
+__device__ __forceinline__ void rescale(State<D>& st, float f) {
   if (__ballot(f != 1.0f)) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < Dim<D>::kDB; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) st.acc[db][i] *= f;
   }
 }
 
 // O^T += V^T P^T for one tile; vbuf holds the decoded, transposed V tile.
-__device__ __forceinline__ void pv_tile(const uint8_t* vbuf, int c, int hf, const half8_t (&pb)[2][2], State& st) {
+template <int D>
+__device__ __forceinline__ void pv_tile(const uint8_t* vbuf, int c, int hf, const half8_t (&pb)[2][2], State<D>& st) {
   const uint8_t* va = vbuf + c * kVRow + 16 * hf;
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < Dim<D>::kDB; ++db)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const half8_t a = *reinterpret_cast<const half8_t*>(va + (32 * db) * kVRow + 64 * b + 32 * u);
@@ -322,9 +372,13 @@ struct Ctx {
 // one iteration earlier), after which K t+3 and V t+2 are loaded.  Buffers:
 // K and V tile u live in buffer u & 1; a tile is decoded one iteration after
 // the buffer's previous tile was last read, with one barrier per iteration.
-template <bool MASK>
-__device__ __forceinline__ void step(const Ctx& x, int t, const half8_t (&qf)[8], const Geo& geo, Raw& raw,
-                                     float16_t (&scur)[2], State& st) {
+template <bool MASK, int D>
+__device__ __forceinline__ void step(const Ctx& x, int t, const half8_t (&qf)[Dim<D>::kSteps], const Geo& geo,
+                                     Raw<D>& raw, float16_t (&scur)[2], State<D>& st) {
+  constexpr int kBuf = Dim<D>::kBuf;
+  // VALU instructions placed after each MFMA of the score product: the
+  // softmax work of a tile does not depend on D, the MFMA count does
+  constexpr int kVpm = 5 * 128 / D;
   uint8_t* b0 = x.smem + (t & 1) * kBuf;        // K t+2 (write), V t (read)
   uint8_t* b1 = x.smem + ((t + 1) & 1) * kBuf;  // K t+1 (read), V t+1 (write)
   const int key0 = tile_key0(t, x.tpb, x.fb_keys);
@@ -340,28 +394,28 @@ __device__ __forceinline__ void step(const Ctx& x, int t, const half8_t (&qf)[8]
   // Region 1: scores of tile t+1 (MFMA) under the softmax of tile t (VALU).
   // On the last tile the scores are computed from a stale buffer and unused.
   float16_t snext[2];
-  qk_tile(b1, x.c, x.hf, qf, snext);
+  qk_tile<D>(b1, x.c, x.hf, qf, snext);
   half8_t pb[2][2];
   // keys past the query's limit or past the frame block's end take no part
-  const float f = softmax_tile<MASK>(scur, key0, x.hf, x.cq, min(x.lim, (fb + 1) * x.fb_keys), x.kts[fb], st, pb);
+  const float f = softmax_tile<MASK, D>(scur, key0, x.hf, x.cq, min(x.lim, (fb + 1) * x.fb_keys), x.kts[fb], st, pb);
   __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
+  for (int s = 0; s < Dim<D>::kSteps; ++s) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, kVpm, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, kVpm, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
   rescale(st, f);
   // Region 2: P V of tile t (MFMA) under the decode of K t+2 and V t+1 (VALU
   // and LDS writes).  Buffers past the last tile are rewritten harmlessly.
-  pv_tile(b0 + kKBuf, x.c, x.hf, pb, st);
-  decode_k(raw, b0, x.tid);
-  decode_v(raw, b1, x.tid);
+  pv_tile<D>(b0 + Dim<D>::kKBuf, x.c, x.hf, pb, st);
+  decode_k<D>(raw, b0, x.tid);
+  decode_v<D>(raw, b1, x.tid);
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
+  for (int s = 0; s < D / 8; ++s) {
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
@@ -374,13 +428,15 @@ __device__ __forceinline__ void step(const Ctx& x, int t, const half8_t (&qf)[8]
   scur[1] = snext[1];
 }
 
-template <bool F32OUT>
+template <bool F32OUT, int D>
 __global__ __launch_bounds__(256, 2) void kv_attention_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ks,
     const float* __restrict__ kts, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
     const float* __restrict__ vts, void* __restrict__ out, int nq, int tokens, int heads, int frames,
     int q_frames, int fb_keys, int qtiles) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Dim<D>::kLds];
+  constexpr int kSteps = Dim<D>::kSteps;
+  constexpr int kBuf = Dim<D>::kBuf;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -405,7 +461,7 @@ __global__ __launch_bounds__(256, 2) void kv_attention_kernel(
   const int kmin_w = (first_frame + qw / tokens + 1) * tokens;
 
   Geo geo{kc, ks, vc, vs, heads, h, nkeys, 0u, {0u, 0u, 0u, 0u}};
-  init_geo(geo, tid);
+  init_geo<D>(geo, tid);
 
   // The lane's query, converted to fp16 with a per-row power-of-two scale;
   // d of MFMA step s is 16s + 8hf + j.
@@ -413,14 +469,14 @@ __global__ __launch_bounds__(256, 2) void kv_attention_kernel(
   const bool qvalid = qi < nq;
   const int64_t qrow = (int64_t)qi * heads + h;
   const int lim = qvalid ? (first_frame + qi / tokens + 1) * tokens : kmax;
-  half8_t qf[8];
+  half8_t qf[kSteps];
   float cq;
   {
-    u32x4_t raw[8];
+    u32x4_t raw[kSteps];
     float mx = 0.0f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      raw[s] = qvalid ? *reinterpret_cast<const u32x4_t*>(q + qrow * kD + 16 * s + 8 * hf) : u32x4_t{0, 0, 0, 0};
+    for (int s = 0; s < kSteps; ++s) {
+      raw[s] = qvalid ? *reinterpret_cast<const u32x4_t*>(q + qrow * D + 16 * s + 8 * hf) : u32x4_t{0, 0, 0, 0};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         mx = fmaxf(mx, fabsf(bf16_to_f32(raw[s][j] & 0xFFFFu)));
@@ -435,9 +491,9 @@ __global__ __launch_bounds__(256, 2) void kv_attention_kernel(
       e = min(max(15 - E, -126), 126);  // mx * 2^e in [2^14, 2^15) unless clamped
     }
     const float sc = ldexpf(1.0f, e);
-    cq = ldexpf(kLog2eRsqrtD, -e);
+    cq = ldexpf(Dim<D>::kLog2eRsqrtD, -e);
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int s = 0; s < kSteps; ++s)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         qf[s][2 * j] = (_Float16)(bf16_to_f32(raw[s][j] & 0xFFFFu) * sc);
@@ -445,31 +501,31 @@ __global__ __launch_bounds__(256, 2) void kv_attention_kernel(
       }
   }
 
-  State st;
+  State<D> st;
   st.m = kMInit;
   st.l = 0.0f;
   st.svref = 0.0f;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < Dim<D>::kDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) st.acc[db][i] = 0.0f;
 
   // Prologue: K and V tile 0 and K tile 1 decoded, the scores of tile 0
   // computed, raw codes of K tile 2 and V tile 1 in flight.
-  Raw raw;
-  load_raw_k(geo, 0, tid, raw);
-  load_raw_v(geo, 0, tid, raw);
-  decode_k(raw, smem, tid);
-  decode_v(raw, smem, tid);
+  Raw<D> raw;
+  load_raw_k<D>(geo, 0, tid, raw);
+  load_raw_v<D>(geo, 0, tid, raw);
+  decode_k<D>(raw, smem, tid);
+  decode_v<D>(raw, smem, tid);
   if (nt > 1) {
-    load_raw_k(geo, tile_key0(1, tpb, fb_keys), tid, raw);
-    decode_k(raw, smem + kBuf, tid);
+    load_raw_k<D>(geo, tile_key0(1, tpb, fb_keys), tid, raw);
+    decode_k<D>(raw, smem + kBuf, tid);
   }
-  if (nt > 2) load_raw_k(geo, tile_key0(2, tpb, fb_keys), tid, raw);
-  if (nt > 1) load_raw_v(geo, tile_key0(1, tpb, fb_keys), tid, raw);
+  if (nt > 2) load_raw_k<D>(geo, tile_key0(2, tpb, fb_keys), tid, raw);
+  if (nt > 1) load_raw_v<D>(geo, tile_key0(1, tpb, fb_keys), tid, raw);
   __syncthreads();
   float16_t scur[2];
-  qk_tile(smem, c, hf, qf, scur);
+  qk_tile<D>(smem, c, hf, qf, scur);
   __syncthreads();   // K tile 0 is read: its buffer is rewritten in the first iteration
 
   // Tiles wholly below this wavefront's first query limit need no mask; the
@@ -481,14 +537,14 @@ __global__ __launch_bounds__(256, 2) void kv_attention_kernel(
   int nt_plain = min(kmin_w / kKT, nt);
   if (tpb * kKT != fb_keys) nt_plain = min(nt_plain, tpb - 1);
   int t = 0;
-  for (; t < nt_plain; ++t) step<false>(cx, t, qf, geo, raw, scur, st);
-  for (; t < nt; ++t) step<true>(cx, t, qf, geo, raw, scur, st);
+  for (; t < nt_plain; ++t) step<false, D>(cx, t, qf, geo, raw, scur, st);
+  for (; t < nt; ++t) step<true, D>(cx, t, qf, geo, raw, scur, st);
 
   const float l = st.l + __shfl_xor(st.l, 32, 64);
   const float a = st.svref / l;
   if (!qvalid) return;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < Dim<D>::kDB; ++db)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int d = 32 * db + 8 * i4 + 4 * hf;
@@ -496,32 +552,44 @@ __global__ __launch_bounds__(256, 2) void kv_attention_kernel(
       const float v2 = st.acc[db][4 * i4 + 2] * a, v3 = st.acc[db][4 * i4 + 3] * a;
       if constexpr (F32OUT) {
         float4_t wv = {v0, v1, v2, v3};
-        *reinterpret_cast<float4_t*>(static_cast<float*>(out) + qrow * kD + d) = wv;
+        *reinterpret_cast<float4_t*>(static_cast<float*>(out) + qrow * D + d) = wv;
       } else {
         u32x2_t wv;
         wv[0] = f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16);
         wv[1] = f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16);
-        *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + qrow * kD + d) = wv;
+        *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + qrow * D + d) = wv;
       }
     }
+}
+
+template <int D>
+void launch_dim(const uint16_t* q, QOut k, QOut v, void* out, int out_f32, int nq, int tokens, int heads,
+                int frames, int q_frames, int fb_keys, int qtiles, hipStream_t s) {
+  const int grid = qtiles * heads;
+  if (out_f32)
+    kv_attention_kernel<true, D><<<grid, 256, 0, s>>>(q, k.codes, k.scales, k.tscale, v.codes, v.scales, v.tscale,
+                                                      out, nq, tokens, heads, frames, q_frames, fb_keys, qtiles);
+  else
+    kv_attention_kernel<false, D><<<grid, 256, 0, s>>>(q, k.codes, k.scales, k.tscale, v.codes, v.scales,
+                                                       v.tscale, out, nq, tokens, heads, frames, q_frames, fb_keys,
+                                                       qtiles);
 }
 
 }  // namespace
 
 hipError_t launch_kv_attention(const uint16_t* q, QOut k, QOut v, void* out, int out_f32, int64_t nq, int64_t tokens,
-                               int64_t heads, int64_t frames, int64_t q_frames, int64_t frame_block,
-                               hipStream_t s) {
+                               int64_t heads, int64_t head_dim, int64_t frames, int64_t q_frames,
+                               int64_t frame_block, hipStream_t s) {
   const int qtiles = (int)((nq + kQT - 1) / kQT);
-  const int grid = qtiles * (int)heads;
   const int fb_keys = (int)(frame_block * tokens);
-  if (out_f32)
-    kv_attention_kernel<true><<<grid, 256, 0, s>>>(q, k.codes, k.scales, k.tscale, v.codes, v.scales, v.tscale, out,
-                                                   (int)nq, (int)tokens, (int)heads, (int)frames, (int)q_frames,
-                                                   fb_keys, qtiles);
+  if (head_dim == 64)
+    launch_dim<64>(q, k, v, out, out_f32, (int)nq, (int)tokens, (int)heads, (int)frames, (int)q_frames, fb_keys,
+                   qtiles, s);
+  else if (head_dim == 128)
+    launch_dim<128>(q, k, v, out, out_f32, (int)nq, (int)tokens, (int)heads, (int)frames, (int)q_frames, fb_keys,
+                    qtiles, s);
   else
-    kv_attention_kernel<false><<<grid, 256, 0, s>>>(q, k.codes, k.scales, k.tscale, v.codes, v.scales, v.tscale,
-                                                    out, (int)nq, (int)tokens, (int)heads, (int)frames,
-                                                    (int)q_frames, fb_keys, qtiles);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

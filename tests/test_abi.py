@@ -202,7 +202,9 @@ def test_kv_attention_rejects_bad_arguments(nv):
     assert call(fb=0) == EINVAL
     assert call(k=_t(nv, 12 * 40 * 2 - 1, 128)) == EINVAL     # cache rows
     assert call(v=_t(nv, 12 * 40 * 2, 64)) == EINVAL          # head_dim mismatch
-    assert call(k=_t(nv, 12 * 40 * 2, 64), v=_t(nv, 12 * 40 * 2, 64), d=64) == EUNS
+    # head dimensions other than 64 and 128 are refused before any launch
+    for d in (32, 96, 256):
+        assert call(k=_t(nv, 12 * 40 * 2, d), v=_t(nv, 12 * 40 * 2, d), d=d) == EUNS, d
     # zero queries is a no-op, whatever the frame-block size (frame blocks of
     # any key count are supported; GPU tests cover them)
     k13 = _t(nv, 12 * 13 * 2, 128)

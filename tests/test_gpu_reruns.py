@@ -14,7 +14,7 @@ import workloads
 from gpu_helpers import (assert_gemm_close, assert_q_exact, dev_bf16, dev_f32, host_bf16_bits, log, require_gpu,
                          widen)
 from oracle import attention as A
-from test_gpu_attention import _check, _run, _score_bound
+from test_gpu_attention import _check, _run, _score_bound, _underflow_term
 
 pytestmark = pytest.mark.gpu
 
@@ -83,4 +83,5 @@ def test_window_attention_reruns(nv, shift):
     qf = widen(w["q"]).reshape(q_frames * tokens, heads, d)
     ref, scale = A.window_attention_ref(qf, kq, vq, frames, tokens, heads, d, q_frames, fb, query_rows=rows)
     bound = _score_bound(qf, kq, frames, tokens, heads, d, q_frames, fb, rows)
-    _check(g16[rows], ref, scale, bound, True, f"seed +{shift}")
+    under = _underflow_term(qf, kq, vq, frames, tokens, heads, d, q_frames, fb, rows, ref)
+    _check(g16[rows], ref, scale, bound, True, f"seed +{shift}", under)
