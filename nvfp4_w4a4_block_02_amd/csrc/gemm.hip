@@ -154,12 +154,12 @@ __device__ __forceinline__ void compute_tile(const Frags<FA, FB>& t, float16_t (
 // lane, the row offsets (uniform multiples of ldc) added per accumulator row
 // and the column fragments as immediate store offsets; edge sub-tiles check
 // every element.  Both store the same values.
-template <int FA, int FB, int OUT, int EPI>
+template <int FA, int FB, int OUT, int EPI, bool WHOLE = false>
 __device__ __forceinline__ void store_tile(const float16_t (&acc)[FA][FB], float sab, int m0, int n0, int li, int hh,
                                            int M, int N, void* __restrict__ c, int64_t ldc, float* __restrict__ amax_out) {
   using T = typename std::conditional<OUT == 0, float, uint16_t>::type;
   float mx = 0.0f;
-  if (m0 + 32 * FA <= M && n0 + 32 * FB <= N) {
+  if (WHOLE || (m0 + 32 * FA <= M && n0 + 32 * FB <= N)) {
     T* const base = static_cast<T*>(c) + (int64_t)(m0 + hh * 4) * ldc + n0 + li;
 #pragma unroll
     for (int i = 0; i < FA; ++i) {
@@ -187,6 +187,7 @@ __device__ __forceinline__ void store_tile(const float16_t (&acc)[FA][FB], float
     }
     return;
   }
+  if constexpr (WHOLE) return;
 #pragma unroll
   for (int i = 0; i < FA; ++i) {
 #pragma unroll
@@ -412,7 +413,7 @@ __device__ __forceinline__ void store_tile_staged(const float16_t (&acc)[FA][FB]
 //      when t % 4 == 1 the loads of scale group (t+3)/4;
 //   3. 8 MFMA steps on tile t, each overlapped with the decode of the next
 //      step and the code loads of tile t+3 into stage t % 3.
-template <int FA, int FB, int OUT, int EPI>
+template <int FA, int FB, int OUT, int EPI, bool WHOLE>
 __global__ __launch_bounds__(256) void gemm_lds_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts,
@@ -581,7 +582,7 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
       return;
     }
   }
-  store_tile<FA, FB, OUT, EPI>(acc, sab, m0, n0, li, hh, M, N, c, ldc, amax_out);
+  store_tile<FA, FB, OUT, EPI, WHOLE>(acc, sab, m0, n0, li, hh, M, N, c, ldc, amax_out);
 }
 
 // ---------------------------------------------------------------------------
@@ -653,7 +654,19 @@ template <int FA, int FB, int OUT, int EPI>
 void launch_lds(const Args& g, hipStream_t s) {
   const int tiles_m = (g.m + 64 * FA - 1) / (64 * FA), tiles_n = (g.n + 64 * FB - 1) / (64 * FB);
   const int band = band_for(tiles_m, tiles_n, 64 * FA, 64 * FB);
-  gemm_lds_kernel<FA, FB, OUT, EPI><<<tiles_m * tiles_n, 256, 0, s>>>(
+  // Launches of whole tiles only (no tile reaches past M or N) of the
+  // 4x4 float32-output kernels take an instance without the edge path:
+  // with it, all 256 accumulators are copied to vector registers ahead of
+  // the branch between the two paths, which spills.
+  if constexpr (OUT == 0 && FA * FB >= 16) {
+    if (g.m % (64 * FA) == 0 && g.n % (64 * FB) == 0) {
+      gemm_lds_kernel<FA, FB, OUT, EPI, true><<<tiles_m * tiles_n, 256, 0, s>>>(
+          g.a.codes, g.a.scales, g.a.tscale, g.b.codes, g.b.scales, g.b.tscale, g.c, g.ldc, g.m, g.n, g.k, g.amax,
+          band);
+      return;
+    }
+  }
+  gemm_lds_kernel<FA, FB, OUT, EPI, false><<<tiles_m * tiles_n, 256, 0, s>>>(
       g.a.codes, g.a.scales, g.a.tscale, g.b.codes, g.b.scales, g.b.tscale, g.c, g.ldc, g.m, g.n, g.k, g.amax, band);
 }
 

@@ -185,6 +185,28 @@ def test_gelu_epilogue_and_amax(nv, m, n, k):
     assert amax.item() == float(np.abs(h.cpu().numpy()).max())
 
 
+def test_whole_tile_instances_match_edge_instances(nv):
+    """Launches made only of whole 256 x 256 tiles run the 4x4 float32-output
+    kernels without their edge path.  The same rows computed inside a launch
+    with a ragged tile row (edge path present) are bit-identical, plain and
+    with the GELU epilogue and its amax; the whole-tile result also meets
+    the float64 oracle."""
+    m, n, k = 512, 768, 1024
+    log(f"gemm whole-tile instances {m}x{n}x{k}")
+    rng = np.random.default_rng(512768)
+    ga, gb, oa, ob = _operands(nv, rng, m + 1, n, k)   # one extra A row: the ragged launch
+    whole = nv.NVFP4Tensor(ga.codes[:m], ga.scales[:m], ga.tscale)
+    for epi in (nv.EPI_NONE, nv.EPI_GELU_TANH):
+        amax_w, amax_r = torch.empty(1, device="cuda"), torch.empty(1, device="cuda")
+        cw = nv.gemm(whole, gb, out_dtype=torch.float32, epilogue=epi, amax_out=amax_w, tiles=(4, 4))
+        cr = nv.gemm(ga, gb, out_dtype=torch.float32, epilogue=epi, amax_out=amax_r, tiles=(4, 4))
+        assert torch.equal(cw.view(torch.int32), cr[:m].view(torch.int32)), epi
+        assert amax_w.item() == float(cw.abs().max().item())
+    cref, bound = oracle.gemm_ref(oa, ob, rows=slice(0, m))
+    cw = nv.gemm(whole, gb, out_dtype=torch.float32, tiles=(4, 4))
+    assert_gemm_close(cw.cpu().numpy(), cref, bound, False, "whole tiles")
+
+
 # ---------------------------------------------------------------- workloads
 def _all_rows_close(gpu, oa, ob, out_bf16, tag, chunk=2048, keep=False):
     """Every row of a GPU GEMM result against gemm_ref, the float64 result
