@@ -345,10 +345,10 @@ __device__ __forceinline__ void read_stage(Frags<FA, FB>& fr, const uint8_t* st,
 // keep the region within kOutRegion bytes.  The row pitch is padded by 16
 // bytes so that the two row groups a 2-byte LDS store touches (rows r and
 // r + 4) fall in different banks.
-template <int FA, int FB, int EPI>
+template <int FA, int FB, int EPI, bool CHECKED = false>
 __device__ __forceinline__ void store_tile_staged(const float16_t (&acc)[FA][FB], float sab, int m0, int n0, int l,
                                                   int li, int hh, uint8_t* lds, uint16_t* __restrict__ c,
-                                                  int64_t ldc, float* __restrict__ amax_out) {
+                                                  int64_t ldc, float* __restrict__ amax_out, int M = 0, int N = 0) {
   constexpr int COLS = 32 * FB, PITCH = 2 * COLS + 16;
   constexpr int IC = (FA * 32 * PITCH <= kOutRegion) ? FA : 2;  // fragment rows per pass
   static_assert(FA % IC == 0 && IC * 32 * PITCH <= kOutRegion, "staging region");
@@ -379,7 +379,8 @@ __device__ __forceinline__ void store_tile_staged(const float16_t (&acc)[FA][FB]
     for (int it = 0; it < IC * 32 / RPI; ++it) {
       const int row = it * RPI + l / LPR, seg = l % LPR;
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + row * PITCH + 16 * seg);
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(c + (int64_t)(m0 + 32 * i0 + row) * ldc + n0 + 8 * seg));
+      if (!CHECKED || (m0 + 32 * i0 + row < M && n0 + 8 * seg < N))
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(c + (int64_t)(m0 + 32 * i0 + row) * ldc + n0 + 8 * seg));
     }
     if (i0 + IC < FA) {
       wait_lgkmcnt0();
@@ -413,7 +414,7 @@ __device__ __forceinline__ void store_tile_staged(const float16_t (&acc)[FA][FB]
 //      when t % 4 == 1 the loads of scale group (t+3)/4;
 //   3. 8 MFMA steps on tile t, each overlapped with the decode of the next
 //      step and the code loads of tile t+3 into stage t % 3.
-template <int FA, int FB, int OUT, int EPI, bool WHOLE>
+template <int FA, int FB, int OUT, int EPI, int EDGE>
 __global__ __launch_bounds__(256) void gemm_lds_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts,
@@ -574,15 +575,22 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
     // Every wave has finished with the LDS ring (its loads landed, its reads
     // done) before any wave overwrites it with output.
     __syncthreads();
-    const bool whole = m0 + 32 * FA <= M && n0 + 32 * FB <= N && ldc % 8 == 0 && ((uintptr_t)c & 15) == 0;
     static_assert(4 * kOutRegion <= SMEM, "the staging regions reuse the LDS rings");
+    if constexpr (EDGE != 0) {
+      // the host checked ldc % 8, the alignment of C and N % 8: edge tiles
+      // (EDGE 2) store only their rows below M and 8-column pieces below N
+      store_tile_staged<FA, FB, EPI, EDGE == 2>(acc, sab, m0, n0, l, li, hh, smem + wave * kOutRegion,
+                                                static_cast<uint16_t*>(c), ldc, amax_out, M, N);
+      return;
+    }
+    const bool whole = m0 + 32 * FA <= M && n0 + 32 * FB <= N && ldc % 8 == 0 && ((uintptr_t)c & 15) == 0;
     if (whole) {
       store_tile_staged<FA, FB, EPI>(acc, sab, m0, n0, l, li, hh, smem + wave * kOutRegion, static_cast<uint16_t*>(c),
                                      ldc, amax_out);
       return;
     }
   }
-  store_tile<FA, FB, OUT, EPI, WHOLE>(acc, sab, m0, n0, li, hh, M, N, c, ldc, amax_out);
+  if constexpr (!kStaged || EDGE == 0) store_tile<FA, FB, OUT, EPI, EDGE == 1>(acc, sab, m0, n0, li, hh, M, N, c, ldc, amax_out);
 }
 
 // ---------------------------------------------------------------------------
@@ -654,20 +662,28 @@ template <int FA, int FB, int OUT, int EPI>
 void launch_lds(const Args& g, hipStream_t s) {
   const int tiles_m = (g.m + 64 * FA - 1) / (64 * FA), tiles_n = (g.n + 64 * FB - 1) / (64 * FB);
   const int band = band_for(tiles_m, tiles_n, 64 * FA, 64 * FB);
-  // Launches of whole tiles only (no tile reaches past M or N) of the
-  // 4x4 float32-output kernels take an instance without the edge path:
-  // with it, all 256 accumulators are copied to vector registers ahead of
-  // the branch between the two paths, which spills.
-  if constexpr (OUT == 0 && FA * FB >= 16) {
-    if (g.m % (64 * FA) == 0 && g.n % (64 * FB) == 0) {
-      gemm_lds_kernel<FA, FB, OUT, EPI, true><<<tiles_m * tiles_n, 256, 0, s>>>(
-          g.a.codes, g.a.scales, g.a.tscale, g.b.codes, g.b.scales, g.b.tscale, g.c, g.ldc, g.m, g.n, g.k, g.amax,
-          band);
-      return;
+  // The 4x4 kernels get instances without the branch between their two
+  // epilogue paths when the launch allows it: with the branch, all 256
+  // accumulators are copied to vector registers ahead of it, which spills.
+  // Float32 output: a launch of whole tiles only (no tile reaches past M or
+  // N) needs no edge path (EDGE 1).  bf16 output (staged through LDS): with
+  // ldc % 8 == 0, C 16-byte aligned and N % 8 == 0 the staged path stores
+  // edge tiles too, checking rows and 8-column pieces (EDGE 2; EDGE 1
+  // without the checks when every tile is whole).
+  const bool whole = g.m % (64 * FA) == 0 && g.n % (64 * FB) == 0;
+  auto go = [&](auto edge) {
+    gemm_lds_kernel<FA, FB, OUT, EPI, decltype(edge)::value><<<tiles_m * tiles_n, 256, 0, s>>>(
+        g.a.codes, g.a.scales, g.a.tscale, g.b.codes, g.b.scales, g.b.tscale, g.c, g.ldc, g.m, g.n, g.k, g.amax, band);
+  };
+  if constexpr (FA * FB >= 16) {
+    if constexpr (OUT == 0) {
+      if (whole) return go(std::integral_constant<int, 1>());
+    } else {
+      if (g.ldc % 8 == 0 && ((uintptr_t)g.c & 15) == 0 && g.n % 8 == 0)
+        return whole ? go(std::integral_constant<int, 1>()) : go(std::integral_constant<int, 2>());
     }
   }
-  gemm_lds_kernel<FA, FB, OUT, EPI, false><<<tiles_m * tiles_n, 256, 0, s>>>(
-      g.a.codes, g.a.scales, g.a.tscale, g.b.codes, g.b.scales, g.b.tscale, g.c, g.ldc, g.m, g.n, g.k, g.amax, band);
+  go(std::integral_constant<int, 0>());
 }
 
 template <int OUT, int EPI>

@@ -186,13 +186,16 @@ def test_gelu_epilogue_and_amax(nv, m, n, k):
 
 
 def test_whole_tile_instances_match_edge_instances(nv):
-    """Launches made only of whole 256 x 256 tiles run the 4x4 float32-output
-    kernels without their edge path.  The same rows computed inside a launch
-    with a ragged tile row (edge path present) are bit-identical, plain and
-    with the GELU epilogue and its amax; the whole-tile result also meets
-    the float64 oracle."""
+    """The 4x4 kernels have instances without the branch between their two
+    epilogue paths: float32 output for launches of whole 256 x 256 tiles,
+    bf16 output (staged) for whole tiles and, with row and column checks,
+    for edge tiles when ldc % 8 == 0 and N % 8 == 0.  Each is bit-identical
+    to the general instance on the same rows (plain and with the GELU
+    epilogue and its amax): a launch with one extra A row has a ragged tile
+    row, and a bf16 output with a row pitch of n + 4 takes the general
+    instance.  The whole-tile result also meets the float64 oracle."""
     m, n, k = 512, 768, 1024
-    log(f"gemm whole-tile instances {m}x{n}x{k}")
+    log(f"gemm whole-tile and edge instances {m}x{n}x{k}")
     rng = np.random.default_rng(512768)
     ga, gb, oa, ob = _operands(nv, rng, m + 1, n, k)   # one extra A row: the ragged launch
     whole = nv.NVFP4Tensor(ga.codes[:m], ga.scales[:m], ga.tscale)
@@ -202,6 +205,17 @@ def test_whole_tile_instances_match_edge_instances(nv):
         cr = nv.gemm(ga, gb, out_dtype=torch.float32, epilogue=epi, amax_out=amax_r, tiles=(4, 4))
         assert torch.equal(cw.view(torch.int32), cr[:m].view(torch.int32)), epi
         assert amax_w.item() == float(cw.abs().max().item())
+        # bf16: whole tiles (no checks), edge tiles (checked staged stores),
+        # and the general instance through a row pitch that is not a multiple of 8
+        amax_s = torch.empty(1, device="cuda")
+        hw = nv.gemm(whole, gb, out_dtype=torch.bfloat16, epilogue=epi, amax_out=amax_w, tiles=(4, 4))
+        hr = nv.gemm(ga, gb, out_dtype=torch.bfloat16, epilogue=epi, amax_out=amax_r, tiles=(4, 4))
+        big = torch.full((m + 1, n + 4), 7.0, dtype=torch.bfloat16, device="cuda")
+        nv.gemm(ga, gb, out=big[:, :n], epilogue=epi, amax_out=amax_s, tiles=(4, 4))
+        assert torch.equal(hr.view(torch.int16), big[:, :n].view(torch.int16)), epi
+        assert torch.equal(hw.view(torch.int16), hr[:m].view(torch.int16)), epi
+        assert bool((big[:, n:] == 7.0).all())
+        assert amax_r.item() == amax_s.item() == float(hr.float().abs().max().item())
     cref, bound = oracle.gemm_ref(oa, ob, rows=slice(0, m))
     cw = nv.gemm(whole, gb, out_dtype=torch.float32, tiles=(4, 4))
     assert_gemm_close(cw.cpu().numpy(), cref, bound, False, "whole tiles")
