@@ -154,9 +154,15 @@ __device__ __forceinline__ void compute_tile(const Frags<FA, FB>& t, float16_t (
 // lane, the row offsets (uniform multiples of ldc) added per accumulator row
 // and the column fragments as immediate store offsets; edge sub-tiles check
 // every element.  Both store the same values.
+// This lane's index in its wavefront from mbcnt, for epilogues that should
+// not keep the thread id in a register through the K loop.
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// l: this lane's index in its wavefront (li = l % 32, hh = l / 32).
 template <int FA, int FB, int OUT, int EPI, bool WHOLE = false>
-__device__ __forceinline__ void store_tile(const float16_t (&acc)[FA][FB], float sab, int m0, int n0, int li, int hh,
-                                           int M, int N, void* __restrict__ c, int64_t ldc, float* __restrict__ amax_out) {
+__device__ __forceinline__ void store_tile(const float16_t (&acc)[FA][FB], float sab, int m0, int n0, int l, int li,
+                                           int hh, int M, int N, void* __restrict__ c, int64_t ldc,
+                                           float* __restrict__ amax_out) {
   using T = typename std::conditional<OUT == 0, float, uint16_t>::type;
   float mx = 0.0f;
   if (WHOLE || (m0 + 32 * FA <= M && n0 + 32 * FB <= N)) {
@@ -183,7 +189,7 @@ __device__ __forceinline__ void store_tile(const float16_t (&acc)[FA][FB], float
     }
     if (amax_out != nullptr) {
       mx = wave_max(mx);
-      if ((threadIdx.x & 63) == 0 && mx > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(amax_out), __float_as_uint(mx));
+      if (l == 0 && mx > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(amax_out), __float_as_uint(mx));
     }
     return;
   }
@@ -213,7 +219,7 @@ __device__ __forceinline__ void store_tile(const float16_t (&acc)[FA][FB], float
   }
   if (amax_out != nullptr) {
     mx = wave_max(mx);
-    if ((threadIdx.x & 63) == 0 && mx > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(amax_out), __float_as_uint(mx));
+    if (l == 0 && mx > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(amax_out), __float_as_uint(mx));
   }
 }
 
@@ -389,7 +395,7 @@ __device__ __forceinline__ void store_tile_staged(const float16_t (&acc)[FA][FB]
   }
   if (amax_out != nullptr) {
     mx = wave_max(mx);
-    if ((threadIdx.x & 63) == 0 && mx > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(amax_out), __float_as_uint(mx));
+    if (l == 0 && mx > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(amax_out), __float_as_uint(mx));
   }
 }
 
@@ -571,6 +577,11 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
   wait_vmcnt<0>();  // no load into LDS may be in flight when the workgroup ends
 
   const int m0 = mwg + wy * 32 * FA, n0 = nwg + wx * 32 * FB;
+  {
+  // The instances without a second epilogue path recompute the lane index
+  // here: kept through the K loop it is spilled to scratch (the loop uses
+  // all 256 VGPRs) and its reload waits behind the tile's stores.
+  const int le = EDGE != 0 ? lane_id() : l, li = le & 31, hh = le >> 5;
   if constexpr (kStaged) {
     // Every wave has finished with the LDS ring (its loads landed, its reads
     // done) before any wave overwrites it with output.
@@ -579,18 +590,20 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
     if constexpr (EDGE != 0) {
       // the host checked ldc % 8, the alignment of C and N % 8: edge tiles
       // (EDGE 2) store only their rows below M and 8-column pieces below N
-      store_tile_staged<FA, FB, EPI, EDGE == 2>(acc, sab, m0, n0, l, li, hh, smem + wave * kOutRegion,
+      store_tile_staged<FA, FB, EPI, EDGE == 2>(acc, sab, m0, n0, le, li, hh, smem + wave * kOutRegion,
                                                 static_cast<uint16_t*>(c), ldc, amax_out, M, N);
       return;
     }
     const bool whole = m0 + 32 * FA <= M && n0 + 32 * FB <= N && ldc % 8 == 0 && ((uintptr_t)c & 15) == 0;
     if (whole) {
-      store_tile_staged<FA, FB, EPI>(acc, sab, m0, n0, l, li, hh, smem + wave * kOutRegion, static_cast<uint16_t*>(c),
+      store_tile_staged<FA, FB, EPI>(acc, sab, m0, n0, le, li, hh, smem + wave * kOutRegion, static_cast<uint16_t*>(c),
                                      ldc, amax_out);
       return;
     }
   }
-  if constexpr (!kStaged || EDGE == 0) store_tile<FA, FB, OUT, EPI, EDGE == 1>(acc, sab, m0, n0, li, hh, M, N, c, ldc, amax_out);
+  if constexpr (!kStaged || EDGE == 0)
+    store_tile<FA, FB, OUT, EPI, EDGE == 1>(acc, sab, m0, n0, le, li, hh, M, N, c, ldc, amax_out);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -634,7 +647,7 @@ __global__ __launch_bounds__(256) void gemm_checked_kernel(
     load_frags_checked(fr, pa, psa, pb, psb, kt, hh, K);
     compute_tile(fr, acc);
   }
-  store_tile<FA, FB, OUT, EPI>(acc, ats[0] * bts[0], m0, n0, li, hh, M, N, c, ldc, amax_out);
+  store_tile<FA, FB, OUT, EPI>(acc, ats[0] * bts[0], m0, n0, lane, li, hh, M, N, c, ldc, amax_out);
 }
 
 struct Args {
