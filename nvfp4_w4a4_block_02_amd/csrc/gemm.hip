@@ -675,26 +675,25 @@ template <int FA, int FB, int OUT, int EPI>
 void launch_lds(const Args& g, hipStream_t s) {
   const int tiles_m = (g.m + 64 * FA - 1) / (64 * FA), tiles_n = (g.n + 64 * FB - 1) / (64 * FB);
   const int band = band_for(tiles_m, tiles_n, 64 * FA, 64 * FB);
-  // The 4x4 kernels get instances without the branch between their two
-  // epilogue paths when the launch allows it: with the branch, all 256
-  // accumulators are copied to vector registers ahead of it, which spills.
-  // Float32 output: a launch of whole tiles only (no tile reaches past M or
-  // N) needs no edge path (EDGE 1).  bf16 output (staged through LDS): with
-  // ldc % 8 == 0, C 16-byte aligned and N % 8 == 0 the staged path stores
-  // edge tiles too, checking rows and 8-column pieces (EDGE 2; EDGE 1
+  // Instances without the branch between two epilogue paths when the launch
+  // allows it: with the branch, all accumulators are copied to vector
+  // registers ahead of it, which spills in the 4x4 kernels.  Float32 output
+  // (4x4): a launch of whole tiles only (no tile reaches past M or N) needs
+  // no edge path (EDGE 1).  bf16 output staged through LDS (FB 2 or 4):
+  // with ldc % 8 == 0, C 16-byte aligned and N % 8 == 0 the staged path
+  // stores edge tiles too, checking rows and 8-column pieces (EDGE 2; EDGE 1
   // without the checks when every tile is whole).
   const bool whole = g.m % (64 * FA) == 0 && g.n % (64 * FB) == 0;
   auto go = [&](auto edge) {
     gemm_lds_kernel<FA, FB, OUT, EPI, decltype(edge)::value><<<tiles_m * tiles_n, 256, 0, s>>>(
         g.a.codes, g.a.scales, g.a.tscale, g.b.codes, g.b.scales, g.b.tscale, g.c, g.ldc, g.m, g.n, g.k, g.amax, band);
   };
-  if constexpr (FA * FB >= 16) {
-    if constexpr (OUT == 0) {
-      if (whole) return go(std::integral_constant<int, 1>());
-    } else {
-      if (g.ldc % 8 == 0 && ((uintptr_t)g.c & 15) == 0 && g.n % 8 == 0)
-        return whole ? go(std::integral_constant<int, 1>()) : go(std::integral_constant<int, 2>());
-    }
+  if constexpr (OUT == 0 && FA * FB >= 16) {
+    if (whole) return go(std::integral_constant<int, 1>());
+  }
+  if constexpr (OUT == 1 && (FB == 2 || FB == 4)) {
+    if (g.ldc % 8 == 0 && ((uintptr_t)g.c & 15) == 0 && g.n % 8 == 0)
+      return whole ? go(std::integral_constant<int, 1>()) : go(std::integral_constant<int, 2>());
   }
   go(std::integral_constant<int, 0>());
 }

@@ -185,39 +185,40 @@ def test_gelu_epilogue_and_amax(nv, m, n, k):
     assert amax.item() == float(np.abs(h.cpu().numpy()).max())
 
 
-def test_whole_tile_instances_match_edge_instances(nv):
-    """The 4x4 kernels have instances without the branch between their two
-    epilogue paths: float32 output for launches of whole 256 x 256 tiles,
-    bf16 output (staged) for whole tiles and, with row and column checks,
+@pytest.mark.parametrize("tiles", [(4, 4), (2, 4)])
+def test_whole_tile_instances_match_edge_instances(nv, tiles):
+    """Kernel instances without the branch between two epilogue paths: the
+    4x4 float32-output kernels for launches of whole tiles, and the staged
+    bf16 kernels (2x4, 4x4) for whole tiles and, with row and column checks,
     for edge tiles when ldc % 8 == 0 and N % 8 == 0.  Each is bit-identical
     to the general instance on the same rows (plain and with the GELU
     epilogue and its amax): a launch with one extra A row has a ragged tile
     row, and a bf16 output with a row pitch of n + 4 takes the general
     instance.  The whole-tile result also meets the float64 oracle."""
     m, n, k = 512, 768, 1024
-    log(f"gemm whole-tile and edge instances {m}x{n}x{k}")
+    log(f"gemm whole-tile and edge instances {m}x{n}x{k}, tiles {tiles}")
     rng = np.random.default_rng(512768)
     ga, gb, oa, ob = _operands(nv, rng, m + 1, n, k)   # one extra A row: the ragged launch
     whole = nv.NVFP4Tensor(ga.codes[:m], ga.scales[:m], ga.tscale)
     for epi in (nv.EPI_NONE, nv.EPI_GELU_TANH):
         amax_w, amax_r = torch.empty(1, device="cuda"), torch.empty(1, device="cuda")
-        cw = nv.gemm(whole, gb, out_dtype=torch.float32, epilogue=epi, amax_out=amax_w, tiles=(4, 4))
-        cr = nv.gemm(ga, gb, out_dtype=torch.float32, epilogue=epi, amax_out=amax_r, tiles=(4, 4))
+        cw = nv.gemm(whole, gb, out_dtype=torch.float32, epilogue=epi, amax_out=amax_w, tiles=tiles)
+        cr = nv.gemm(ga, gb, out_dtype=torch.float32, epilogue=epi, amax_out=amax_r, tiles=tiles)
         assert torch.equal(cw.view(torch.int32), cr[:m].view(torch.int32)), epi
         assert amax_w.item() == float(cw.abs().max().item())
         # bf16: whole tiles (no checks), edge tiles (checked staged stores),
         # and the general instance through a row pitch that is not a multiple of 8
         amax_s = torch.empty(1, device="cuda")
-        hw = nv.gemm(whole, gb, out_dtype=torch.bfloat16, epilogue=epi, amax_out=amax_w, tiles=(4, 4))
-        hr = nv.gemm(ga, gb, out_dtype=torch.bfloat16, epilogue=epi, amax_out=amax_r, tiles=(4, 4))
+        hw = nv.gemm(whole, gb, out_dtype=torch.bfloat16, epilogue=epi, amax_out=amax_w, tiles=tiles)
+        hr = nv.gemm(ga, gb, out_dtype=torch.bfloat16, epilogue=epi, amax_out=amax_r, tiles=tiles)
         big = torch.full((m + 1, n + 4), 7.0, dtype=torch.bfloat16, device="cuda")
-        nv.gemm(ga, gb, out=big[:, :n], epilogue=epi, amax_out=amax_s, tiles=(4, 4))
+        nv.gemm(ga, gb, out=big[:, :n], epilogue=epi, amax_out=amax_s, tiles=tiles)
         assert torch.equal(hr.view(torch.int16), big[:, :n].view(torch.int16)), epi
         assert torch.equal(hw.view(torch.int16), hr[:m].view(torch.int16)), epi
         assert bool((big[:, n:] == 7.0).all())
         assert amax_r.item() == amax_s.item() == float(hr.float().abs().max().item())
     cref, bound = oracle.gemm_ref(oa, ob, rows=slice(0, m))
-    cw = nv.gemm(whole, gb, out_dtype=torch.float32, tiles=(4, 4))
+    cw = nv.gemm(whole, gb, out_dtype=torch.float32, tiles=tiles)
     assert_gemm_close(cw.cpu().numpy(), cref, bound, False, "whole tiles")
 
 
