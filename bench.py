@@ -407,6 +407,8 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs, only, settle_ms):
                          "dx": torch.empty((m, k), dtype=torch.bfloat16, device="cuda"),
                          "dw": torch.empty((n, k), dtype=torch.float32, device="cuda"),
                          "ws": nv._workspace(nv.OP_RHT16, m, max(k, n), "cuda"),
+                         "ws1": nv._workspace(nv.OP_RHT16, m, max(k, n), "cuda"),
+                         "ws2": nv._workspace(nv.OP_RHT16, m, max(k, n), "cuda"),
                          "wamax": torch.empty(1, dtype=torch.float32, device="cuda")}
             tsets.append(s)
 

@@ -410,6 +410,19 @@ def ffn(x: torch.Tensor, w1: NVFP4Tensor, w2: NVFP4Tensor, out_dtype=torch.bfloa
     return gemm(hq, w2, out_dtype=out_dtype, out=bufs.get("y"), stream=stream)
 
 
+_SIDE_STREAMS: dict = {}
+
+
+def _side_streams(device: torch.device):
+    """Two streams per device for linear_train's independent chains (default
+    priority, created once)."""
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    if idx not in _SIDE_STREAMS:
+        with torch.cuda.device(idx):
+            _SIDE_STREAMS[idx] = (torch.cuda.Stream(), torch.cuda.Stream())
+    return _SIDE_STREAMS[idx]
+
+
 def linear_train(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, sign_mask: int, bufs: dict | None = None,
                  stream=None):
     """The NVFP4 GEMM triple of one linear layer Y = X W^T in training; each
@@ -421,23 +434,45 @@ def linear_train(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, sign_mask: 
       dx = Q(dY) Q(W^T)^T       (bf16)   dy [M, N]; W quantized along dim 0
       dw = R(dY^T) R(X^T)^T     (f32)    dY and X quantized along dim 0
 
-    Returns (y, dx, dw).  Only sequences C-ABI calls.  Preallocated ``bufs``
-    must give "dyt" / "xt" a K of M rounded up to 256."""
+    Returns (y, dx, dw).  Only sequences C-ABI calls: the three chains are
+    independent but for W's amax, which both of W's encodings use, so they
+    are issued on the caller's stream and two side streams (forked from and
+    joined back into the caller's stream with events), letting the small
+    quantization launches run side by side and beside the GEMMs' tails;
+    results are the same as one stream's.
+    Preallocated ``bufs`` must give "dyt" / "xt" a K of M rounded up to 256;
+    workspaces "ws", "ws1", "ws2" serve the three streams (each large enough
+    for the RHT16 of the larger operand)."""
     b = bufs if bufs is not None else {}
-    xq = quantize(x, axis=1, out=b.get("xq"), ws=b.get("ws"), stream=stream)
-    # W is quantized along both of its dims with one tensor scale: its amax
-    # does not depend on the block direction, so one amax pass serves both.
-    wamax = amax(w, out=b.get("wamax"), ws=b.get("ws"), stream=stream)
-    wq = encode(w, wamax, axis=1, out=b.get("wq"), stream=stream)
-    y = gemm(xq, wq, out_dtype=torch.bfloat16, out=b.get("y"), stream=stream)
-    dyq = quantize(dy, axis=1, out=b.get("dyq"), ws=b.get("ws"), stream=stream)
-    wtq = encode(w, wamax, axis=0, out=b.get("wtq"), stream=stream)
-    dx = gemm(dyq, wtq, out_dtype=torch.bfloat16, out=b.get("dx"), stream=stream)
-    # The weight gradient reduces over M; its operands are zero-padded to a
-    # multiple of 256 along M (exact: zero blocks add nothing) so that the
-    # GEMM runs its pipelined path for any token count.
+    s0 = stream if stream is not None else torch.cuda.current_stream()
+    s1, s2 = _side_streams(x.device)
+    fork = torch.cuda.Event()
+    fork.record(s0)
+    s1.wait_event(fork)
+    s2.wait_event(fork)
+    # Chain 1 (caller's stream): W's amax (one tensor scale for both of its
+    # encodings: the amax does not depend on the block direction), W along
+    # K, X along K, then Y.
+    wamax = amax(w, out=b.get("wamax"), ws=b.get("ws"), stream=s0)
+    w_amax_done = torch.cuda.Event()
+    w_amax_done.record(s0)
+    wq = encode(w, wamax, axis=1, out=b.get("wq"), stream=s0)
+    xq = quantize(x, axis=1, out=b.get("xq"), ws=b.get("ws"), stream=s0)
+    y = gemm(xq, wq, out_dtype=torch.bfloat16, out=b.get("y"), stream=s0)
+    # Chain 2: dY along N; W along N once its amax is known; then dX.
+    dyq = quantize(dy, axis=1, out=b.get("dyq"), ws=b.get("ws1"), stream=s1)
+    s1.wait_event(w_amax_done)
+    wtq = encode(w, wamax, axis=0, out=b.get("wtq"), stream=s1)
+    dx = gemm(dyq, wtq, out_dtype=torch.bfloat16, out=b.get("dx"), stream=s1)
+    # Chain 3: the weight gradient reduces over M; its operands are
+    # zero-padded to a multiple of 256 along M (exact: zero blocks add
+    # nothing) so that the GEMM runs its pipelined path for any token count.
     mp = -(-x.shape[0] // 256) * 256
-    dyt = rht16_quantize(dy, sign_mask, axis=0, out=b.get("dyt"), ws=b.get("ws"), stream=stream, k_pad=mp)
-    xt = rht16_quantize(x, sign_mask, axis=0, out=b.get("xt"), ws=b.get("ws"), stream=stream, k_pad=mp)
-    dw = gemm(dyt, xt, out_dtype=torch.float32, out=b.get("dw"), stream=stream)
+    dyt = rht16_quantize(dy, sign_mask, axis=0, out=b.get("dyt"), ws=b.get("ws2"), stream=s2, k_pad=mp)
+    xt = rht16_quantize(x, sign_mask, axis=0, out=b.get("xt"), ws=b.get("ws2"), stream=s2, k_pad=mp)
+    dw = gemm(dyt, xt, out_dtype=torch.float32, out=b.get("dw"), stream=s2)
+    for side in (s1, s2):
+        done = torch.cuda.Event()
+        done.record(side)
+        s0.wait_event(done)
     return y, dx, dw

@@ -401,6 +401,43 @@ def _padded_equal(gq, want, k_pad, tag):
 
 
 @pytest.mark.timeout(600)
+def test_linear_train_streams_match_one_stream(nv):
+    """linear_train issues its three chains on three streams; three calls on
+    different inputs, back to back into the same buffers with no
+    synchronization between them, give results bit-identical to the same
+    C-ABI calls issued one after another on one stream."""
+    m, n, k, mask = 640, 512, 768, 0x5A3C
+    log(f"linear_train on three streams {m}x{n}x{k}, three calls back to back")
+    mp = -(-m // 256) * 256
+    bufs = {"xq": nv.NVFP4Tensor.empty(m, k), "wq": nv.NVFP4Tensor.empty(n, k), "dyq": nv.NVFP4Tensor.empty(m, n),
+            "wtq": nv.NVFP4Tensor.empty(k, n), "dyt": nv.NVFP4Tensor.empty(n, mp), "xt": nv.NVFP4Tensor.empty(k, mp),
+            "y": torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
+            "dx": torch.empty((m, k), dtype=torch.bfloat16, device="cuda"),
+            "dw": torch.empty((n, k), dtype=torch.float32, device="cuda"),
+            "wamax": torch.empty(1, dtype=torch.float32, device="cuda")}
+    for nm in ("ws", "ws1", "ws2"):
+        bufs[nm] = nv._workspace(nv.OP_RHT16, m, max(k, n), "cuda")
+    inputs, outs = [], []
+    for i in range(3):
+        d = workloads.train_linear(m=m, n=n, k=k, seed=300 + i)
+        x, w, dy = dev_bf16(d["x"]), dev_f32(d["w"]), dev_bf16(d["dy"])
+        inputs.append((x, w, dy))
+        y, dx, dw = nv.linear_train(x, w, dy, mask, bufs=bufs)
+        outs.append((y.clone(), dx.clone(), dw.clone(), bufs["dyt"].codes.clone(), bufs["xt"].codes.clone()))
+    torch.cuda.synchronize()
+    for i, (x, w, dy) in enumerate(inputs):
+        xq = nv.quantize(x)
+        wamax = nv.amax(w)
+        wq, wtq = nv.encode(w, wamax, axis=1), nv.encode(w, wamax, axis=0)
+        dyq = nv.quantize(dy)
+        dyt = nv.rht16_quantize(dy, mask, axis=0, k_pad=mp)
+        xt = nv.rht16_quantize(x, mask, axis=0, k_pad=mp)
+        ref = (nv.gemm(xq, wq), nv.gemm(dyq, wtq), nv.gemm(dyt, xt, out_dtype=torch.float32), dyt.codes, xt.codes)
+        torch.cuda.synchronize()
+        for got, want, nm in zip(outs[i], ref, ("y", "dx", "dw", "dyt codes", "xt codes")):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), (i, nm)
+
+
 def test_train_linear_triple_full(nv):
     """Workload 6 (the training slice of the attention projection): forward,
     input gradient and weight gradient.  The six operands linear_train
