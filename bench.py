@@ -82,6 +82,9 @@ def _args():
     p.add_argument("--settle-ms", type=float, default=30.0,
                    help="untimed run time after the warmup steps before any timed pass (clock settle)")
     p.add_argument("--sets", type=int, default=13, help="rotating buffer sets")
+    p.add_argument("--calibrate", action="store_true",
+                   help="only time the vendor's dense GEMMs (torch.matmul in bf16, torch._scaled_mm in fp8) "
+                        "at the four W4A4 GEMM shapes, as the practical MFMA ceiling on this part, and exit")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run three 256 MiB device-to-device copies (calibrates the rocprofv3 "
                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count) and exit")
@@ -97,6 +100,63 @@ def copy_probe():
         y.copy_(x)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_each_way": x.numel() * 4, "copies": 3}), flush=True)
+
+
+# The W4A4 GEMM shapes of the timed rows: C[M, N] = A[M, K] . B[N, K]^T.
+GEMM_SHAPES = (("attn_proj", 2640, 3072, 3072), ("ffn_gemm1", 10560, 14336, 3072),
+               ("ffn_gemm2", 10560, 3072, 14336), ("wgrad", 3072, 3072, 16384))
+
+
+def calibrate(steps):
+    """Dense GEMMs of the library PyTorch dispatches to (hipBLASLt on this
+    part) at the W4A4 GEMM shapes, same "TN" operand layout, bf16 in and out,
+    and fp8 (e4m3, per-tensor scales) in with bf16 out.  These have no decode
+    at all; their rates say what the MFMAs sustain on these shapes at the
+    clocks the part runs under such load, beside the datasheet peaks."""
+    import torch
+
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+    out = {"blas_library": str(torch.backends.cuda.preferred_blas_library()), "shapes": {}}
+    for name, m, n, k in GEMM_SHAPES:
+        flops = 2.0 * m * n * k
+        nsets = max(2, min(8, int(1.2e9 // ((m + n) * k * 2 + m * n * 2))))
+        g = torch.Generator(device="cuda").manual_seed(11)
+        sets = [(torch.randn(m, k, device="cuda", generator=g).to(torch.bfloat16),
+                 torch.randn(n, k, device="cuda", generator=g).mul_(0.02).to(torch.bfloat16),
+                 torch.empty(m, n, device="cuda", dtype=torch.bfloat16)) for _ in range(nsets)]
+        rec = {"M": m, "N": n, "K": k}
+
+        def bf16(i):
+            a, b, c = sets[i % nsets]
+            torch.matmul(a, b.t(), out=c)
+
+        _settle(torch, bf16, 30.0)
+        ms = _b2b_ms(torch, stream, bf16, steps)
+        rec["bf16_ms"] = round(ms, 5)
+        rec["bf16_TFLOP/s"] = round(flops / ms / 1e9, 1)
+        rec["bf16_frac_f16_peak"] = round(flops / ms / 1e9 / PEAK_TFLOPS["f16"], 4)
+        try:
+            f8 = [(a.to(torch.float8_e4m3fn), b.to(torch.float8_e4m3fn)) for a, b, _ in sets]
+            one = torch.ones((), device="cuda")
+
+            def fp8(i):
+                a, b = f8[i % nsets]
+                torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+
+            _settle(torch, fp8, 30.0)
+            ms8 = _b2b_ms(torch, stream, fp8, steps)
+            rec["fp8_ms"] = round(ms8, 5)
+            rec["fp8_TFLOP/s"] = round(flops / ms8 / 1e9, 1)
+            rec["fp8_frac_fp8_peak"] = round(flops / ms8 / 1e9 / PEAK_TFLOPS["fp8"], 4)
+            del f8
+        except (RuntimeError, TypeError) as e:  # no fp8 GEMM for this shape or build
+            rec["fp8_error"] = str(e).splitlines()[0][:160]
+        out["shapes"][name] = rec
+        print(json.dumps({name: rec}), flush=True)
+        del sets
+        torch.cuda.empty_cache()
+    print(json.dumps({"calibration": out}), flush=True)
 
 
 def _b2b_ms(torch, stream, fn, n):
@@ -542,6 +602,9 @@ def cpu_baselines(wl, budget_s=4.0):
 
 def main():
     a = _args()
+    if a.calibrate:
+        calibrate(max(a.steps, 20))
+        return
     if a.copy_probe:
         copy_probe()
         return
