@@ -15,7 +15,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from dataclasses import dataclass
+from dataclasses import dataclass, field
 
 import torch
 
@@ -148,6 +148,9 @@ class NVFP4Tensor:
     codes: torch.Tensor
     scales: torch.Tensor
     tscale: torch.Tensor
+    # (codes, scales, tscale, their data pointers, tscale.numel(), C view) of
+    # the last successful check; not part of the value.
+    _cview: tuple | None = field(default=None, init=False, repr=False, compare=False)
 
     @property
     def rows(self) -> int:
@@ -161,7 +164,15 @@ class NVFP4Tensor:
         """The C view; checks first that the three buffers match each other
         (codes [rows, k/2] and scales [rows, k/16] uint8, at least
         `n_domains` float32 tensor scales), so that no kernel reads or writes
-        past them."""
+        past them.  The checked view is kept and handed out again while the
+        same three tensors still sit on the same device memory (a buffer that
+        is replaced, or whose storage moves, is checked again); the C calls
+        only read it."""
+        cv = self._cview
+        if (cv is not None and cv[0] is self.codes and cv[1] is self.scales and cv[2] is self.tscale
+                and n_domains <= cv[4]
+                and cv[3] == (self.codes.data_ptr(), self.scales.data_ptr(), self.tscale.data_ptr())):
+            return cv[5]
         if self.codes.dim() != 2:
             raise ValueError("codes must be 2-D [rows, k/2]")
         _need(self.codes, "codes", dtype=torch.uint8, gpu=False)
@@ -169,7 +180,10 @@ class NVFP4Tensor:
         _need(self.tscale, "tscale", dtype=torch.float32, min_numel=max(n_domains, 1), gpu=False)
         for name, t in (("codes", self.codes), ("scales", self.scales), ("tscale", self.tscale)):
             _on_gpu(t, name)
-        return _CTensor(self.codes.data_ptr(), self.scales.data_ptr(), self.tscale.data_ptr(), self.rows, self.k)
+        ptrs = (self.codes.data_ptr(), self.scales.data_ptr(), self.tscale.data_ptr())
+        view = _CTensor(ptrs[0], ptrs[1], ptrs[2], self.rows, self.k)
+        self._cview = (self.codes, self.scales, self.tscale, ptrs, self.tscale.numel(), view)
+        return view
 
     @staticmethod
     def empty(rows: int, k: int, n_domains: int = 1, device="cuda") -> "NVFP4Tensor":

@@ -279,3 +279,28 @@ def test_product_and_oracle_share_no_code():
             assert "csrc" not in text and "libnvfp4" not in text, f
     wl = open(os.path.join(root, "workloads", "__init__.py"), encoding="utf-8").read()
     assert not re.search(r"^\s*(import|from)\s+(oracle|nvfp4_w4a4_block_02_amd)", wl, re.M)
+
+
+def test_checked_view_is_checked_again_when_a_buffer_changes(nv, monkeypatch):
+    """NVFP4Tensor.c() keeps its checked C view only while the same three
+    tensors sit on the same memory: a replaced buffer is checked again (and a
+    mismatching one refused), a moved storage gives new pointers, and a
+    larger domain count than the checked one is checked again (CPU-only: the
+    device check is switched off for host tensors here)."""
+    monkeypatch.setattr(nv, "_on_gpu", lambda t, name: None)
+    q = nv.NVFP4Tensor(torch.zeros((4, 16), dtype=torch.uint8), torch.zeros((4, 2), dtype=torch.uint8),
+                       torch.zeros((1,), dtype=torch.float32))
+    v1 = q.c()
+    assert q.c() is v1
+    assert (v1.rows, v1.k, v1.codes) == (4, 32, q.codes.data_ptr())
+    q.scales = torch.zeros((4, 1), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="scales"):
+        q.c()
+    q.scales = torch.zeros((4, 2), dtype=torch.uint8)
+    v2 = q.c()
+    assert v2 is not v1 and v2.scales == q.scales.data_ptr()
+    with pytest.raises(ValueError, match="tscale"):
+        q.c(n_domains=2)
+    q.codes.set_(torch.zeros((4, 16), dtype=torch.uint8))
+    v3 = q.c()
+    assert v3 is not v2 and v3.codes == q.codes.data_ptr()
