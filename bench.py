@@ -331,9 +331,8 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs, only, settle_ms):
                           "aq": nv.NVFP4Tensor.empty(m, k, 1, "cuda"), "ws": nv._workspace(nv.OP_QUANTIZE, m, k, "cuda"),
                           "c": torch.empty((m, n), dtype=torch.float32, device="cuda")})
 
-        def tiny(s):
-            nv.quantize(s["a"], out=s["aq"], ws=s["ws"], stream=stream)
-            nv.gemm(s["aq"], s["wq"], out=s["c"], stream=stream)
+        def tiny(s):  # one C call: activation quantize + GEMM (nvfp4_linear)
+            nv.linear(s["a"], s["wq"], xq=s["aq"], ws=s["ws"], out=s["c"], stream=stream)
 
         t = timed(tiny, tsets, max(steps, 20), warmup)
         out["tiny_linear"] = {**flop_row(t, 2.0 * m * n * k), "us": t["ms"] * 1e3}
@@ -353,7 +352,7 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs, only, settle_ms):
             return timed(lambda g: g.replay(), [g], max(steps // 4, 5), max(warmup // 8, 2))["ms"] * 1e3 / GC
 
         out["tiny_linear"]["graph_us"] = graph_us(
-            lambda s: (nv.quantize(s["a"], out=s["aq"], ws=s["ws"]), nv.gemm(s["aq"], s["wq"], out=s["c"])))
+            lambda s: nv.linear(s["a"], s["wq"], xq=s["aq"], ws=s["ws"], out=s["c"]))
         del tsets
     # KV codec: K and V [12, 880, 24, 128] bf16, 8-frame blocks.
     shape = (12, 880, 24, 128)
@@ -368,16 +367,22 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs, only, settle_ms):
                 s[nm] = _dev_bf16(torch, d[nm]).reshape(shape)
                 s[nm + "q"] = nv.NVFP4Tensor.empty(12 * 880 * 24, 128, 2, "cuda")
                 s[nm + "o"] = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
-            s["ws"] = nv._workspace(nv.OP_KV_QUANT, 12, 8, "cuda")
+            s["ws"] = nv._workspace(nv.OP_KV_QUANT_PAIR, 12, 8, "cuda")
             kvsets.append(s)
 
-        def kvq(s):
-            nv.kv_quant(s["k"], out=s["kq"], ws=s["ws"], stream=stream)
-            nv.kv_quant(s["v"], out=s["vq"], ws=s["ws"], stream=stream)
+        # K and V in one call (nvfp4_kv_quant_pair: one amax and one encode
+        # launch for both); the rows also carry the time of two one-tensor
+        # calls (four launches) for comparison.
+        def kvq(s, fo6=False):
+            nv.kv_quant_pair(s["k"], s["v"], k_out=s["kq"], v_out=s["vq"], ws=s["ws"], stream=stream,
+                             four_over_six=fo6)
 
         def kvq6(s):
-            nv.kv_quant(s["k"], out=s["kq"], ws=s["ws"], stream=stream, four_over_six=True)
-            nv.kv_quant(s["v"], out=s["vq"], ws=s["ws"], stream=stream, four_over_six=True)
+            kvq(s, True)
+
+        def kvq_two(s, fo6=False):
+            nv.kv_quant(s["k"], out=s["kq"], ws=s["ws"], stream=stream, four_over_six=fo6)
+            nv.kv_quant(s["v"], out=s["vq"], ws=s["ws"], stream=stream, four_over_six=fo6)
 
         def kvd(s):
             nv.kv_dequant(s["kq"], shape, out=s["ko"], stream=stream)
@@ -385,8 +390,10 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs, only, settle_ms):
 
         if want("kv_quant"):
             out["kv_quant"] = hbm_row(timed(kvq, kvsets, steps, warmup), kv_bytes)
+            out["kv_quant"]["ms_two_calls"] = timed(kvq_two, kvsets, steps, warmup)["ms"]
         if want("kv_quant_4over6"):
             out["kv_quant_4over6"] = hbm_row(timed(kvq6, kvsets, steps, warmup), kv_bytes)
+            out["kv_quant_4over6"]["ms_two_calls"] = timed(lambda s: kvq_two(s, True), kvsets, steps, warmup)["ms"]
         if want("kv_dequant"):
             kvq(kvsets[0]), kvq(kvsets[1]), kvq(kvsets[2]), kvq(kvsets[3])
             out["kv_dequant"] = hbm_row(timed(kvd, kvsets, steps, warmup), kv_bytes)

@@ -85,6 +85,7 @@ extern "C" {
 #define NVFP4_OP_GEMM     2
 #define NVFP4_OP_KV_QUANT 3
 #define NVFP4_OP_AMAX     4
+#define NVFP4_OP_KV_QUANT_PAIR 5
 
 /* An NVFP4 tensor (host struct holding device pointers), layout above. */
 typedef struct {
@@ -102,7 +103,8 @@ int nvfp4_version(void);
 const char *nvfp4_status_string(int status);
 
 /* Bytes of device workspace `op` needs for a rows x cols problem (for
- * NVFP4_OP_KV_QUANT: rows = frames, cols = frame_block; for NVFP4_OP_AMAX:
+ * NVFP4_OP_KV_QUANT and NVFP4_OP_KV_QUANT_PAIR: rows = frames,
+ * cols = frame_block; for NVFP4_OP_AMAX:
  * cols = rows_per_domain).  The workspace holds the partial maxima of the
  * amax pass (4 KiB per scaling domain); it must be 16-byte aligned and its
  * contents on entry do not matter.  Calls that share a workspace must not
@@ -228,6 +230,23 @@ int nvfp4_gemm_tiled(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int 
                      void *stream);
 
 /*
+ * One W4A4 linear layer in one call (tailorednewshub.com, "Inferencia W4A4
+ * NVFP4": the activations are quantized to NVFP4 on the fly and the layer's
+ * GEMM runs on NVFP4 weights): the activation quantize of x [rows, cols]
+ * (float32 or bf16, blocks along cols, i.e. nvfp4_quantize with axis 1)
+ * into xq, then c = epi(xq @ w^T) (nvfp4_gemm with a = xq, b = w).  The
+ * results and the codes left in xq are those of the two calls; every
+ * argument of both is checked before anything is launched (xq must be
+ * rows x cols, w must have k = cols).  ws: >= nvfp4_workspace_bytes(
+ * NVFP4_OP_QUANTIZE, rows, cols).  One host call instead of two, for
+ * latency-bound small layers.
+ */
+int nvfp4_linear(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                 const nvfp4_tensor *w, const nvfp4_tensor *xq, void *c, int c_dtype,
+                 int64_t ldc, int epilogue, float *amax_out, void *ws, size_t ws_bytes,
+                 void *stream);
+
+/*
  * KV-cache quantization in frame blocks (hyper.ai summary of the LongLive-2.0
  * paper, section "方法": the KV cache is quantized per block of eight frames).
  * kv: device bf16 [frames][tokens][heads][head_dim], contiguous.  One tscale
@@ -257,6 +276,23 @@ int nvfp4_kv_quant(const void *kv, int64_t frames, int64_t tokens, int64_t heads
 int nvfp4_kv_quant_4over6(const void *kv, int64_t frames, int64_t tokens, int64_t heads,
                           int64_t head_dim, int64_t frame_block, const nvfp4_tensor *out,
                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * K and V of one cache in one call (the pages quantize both halves of the KV
+ * cache in 8-frame blocks: hyper.ai summary, section "方法"): the same codes,
+ * block scales and tensor scales as nvfp4_kv_quant (four_over_six = 0) or
+ * nvfp4_kv_quant_4over6 (four_over_six = 1) called on k into k_out and on v
+ * into v_out, with the amax pass of both tensors in one launch and the encode
+ * pass of both in another (two launches instead of four).  k and v: device
+ * bf16 [frames][tokens][heads][head_dim], contiguous, same shape.
+ * ws: >= nvfp4_workspace_bytes(NVFP4_OP_KV_QUANT_PAIR, frames, frame_block)
+ * (twice the one-tensor workspace).  Other values of four_over_six return
+ * NVFP4_EINVAL; errors otherwise as nvfp4_kv_quant.
+ */
+int nvfp4_kv_quant_pair(const void *k, const void *v, int64_t frames, int64_t tokens,
+                        int64_t heads, int64_t head_dim, int64_t frame_block, int four_over_six,
+                        const nvfp4_tensor *k_out, const nvfp4_tensor *v_out, void *ws,
+                        size_t ws_bytes, void *stream);
 
 /*
  * KV-cache dequantization of the whole window to bf16 (the pages rebuild the

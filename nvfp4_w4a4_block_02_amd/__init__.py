@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "libnvfp4.so")
 
 F32, BF16 = 0, 1
 EPI_NONE, EPI_GELU_TANH = 0, 1
-OP_QUANTIZE, OP_RHT16, OP_GEMM, OP_KV_QUANT, OP_AMAX = 0, 1, 2, 3, 4
+OP_QUANTIZE, OP_RHT16, OP_GEMM, OP_KV_QUANT, OP_AMAX, OP_KV_QUANT_PAIR = 0, 1, 2, 3, 4, 5
 
 
 class NVFP4Error(RuntimeError):
@@ -60,8 +60,10 @@ def _load():
         "rht16_quantize": (I, [P, I, I64, I64, I64, I, U32, TP, P, SZ, P]),
         "nvfp4_gemm": (I, [TP, TP, P, I, I64, I, P, P, SZ, P]),
         "nvfp4_gemm_tiled": (I, [TP, TP, P, I, I64, I, P, I, I, P]),
+        "nvfp4_linear": (I, [P, I, I64, I64, I64, TP, TP, P, I, I64, I, P, P, SZ, P]),
         "nvfp4_kv_quant": (I, [P, I64, I64, I64, I64, I64, TP, P, SZ, P]),
         "nvfp4_kv_quant_4over6": (I, [P, I64, I64, I64, I64, I64, TP, P, SZ, P]),
+        "nvfp4_kv_quant_pair": (I, [P, P, I64, I64, I64, I64, I64, I, TP, TP, P, SZ, P]),
         "nvfp4_kv_dequant": (I, [TP, I64, I64, I64, I64, I64, P, P]),
         "nvfp4_dequantize": (I, [TP, I64, P, I, P]),
         "nvfp4_kv_attention": (I, [P, I64, TP, TP, I64, I64, I64, I64, I64, P, I, P]),
@@ -90,8 +92,8 @@ def __getattr__(name):  # module attribute `lib` loads the library on first acce
 
 
 EXPORTED = ("nvfp4_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_amax",
-            "nvfp4_encode", "nvfp4_quantize", "nvfp4_quantize_noalloc", "rht16_quantize", "nvfp4_gemm", "nvfp4_gemm_tiled", "nvfp4_kv_quant",
-            "nvfp4_kv_quant_4over6", "nvfp4_kv_dequant", "nvfp4_dequantize", "nvfp4_kv_attention")
+            "nvfp4_encode", "nvfp4_quantize", "nvfp4_quantize_noalloc", "rht16_quantize", "nvfp4_gemm", "nvfp4_gemm_tiled", "nvfp4_linear", "nvfp4_kv_quant",
+            "nvfp4_kv_quant_4over6", "nvfp4_kv_quant_pair", "nvfp4_kv_dequant", "nvfp4_dequantize", "nvfp4_kv_attention")
 
 
 def _check(status: int, what: str):
@@ -346,6 +348,33 @@ def kv_quant(kv: torch.Tensor, frame_block: int = 8, out: NVFP4Tensor | None = N
     return out
 
 
+def kv_quant_pair(k: torch.Tensor, v: torch.Tensor, frame_block: int = 8, k_out: NVFP4Tensor | None = None,
+                  v_out: NVFP4Tensor | None = None, ws: torch.Tensor | None = None, stream=None,
+                  four_over_six: bool = False) -> tuple[NVFP4Tensor, NVFP4Tensor]:
+    """K and V of one cache in one call (nvfp4_kv_quant_pair): the same results
+    as kv_quant on each, in two launches instead of four."""
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4:
+            raise TypeError(f"{name} must be a contiguous bfloat16 tensor [frames, tokens, heads, head_dim]")
+        _on_gpu(t, name)
+    if k.shape != v.shape:
+        raise ValueError(f"k and v must have the same shape, got {tuple(k.shape)} and {tuple(v.shape)}")
+    f, t, h, d = k.shape
+    nd = -(-f // frame_block) if frame_block > 0 else 1
+    if k_out is None:
+        k_out = NVFP4Tensor.empty(f * t * h, d, nd, k.device)
+    if v_out is None:
+        v_out = NVFP4Tensor.empty(f * t * h, d, nd, k.device)
+    if ws is None:
+        ws = _workspace(OP_KV_QUANT_PAIR, f, frame_block, k.device)
+    _need(ws, "ws")
+    ck, cv = k_out.c(nd), v_out.c(nd)
+    _check(_lib().nvfp4_kv_quant_pair(_ptr(k), _ptr(v), f, t, h, d, frame_block, int(four_over_six),
+                                      ctypes.byref(ck), ctypes.byref(cv), _ptr(ws), ws.numel() * 4,
+                                      _stream(stream)), "nvfp4_kv_quant_pair")
+    return k_out, v_out
+
+
 def kv_dequant(q: NVFP4Tensor, shape, frame_block: int = 8, out: torch.Tensor | None = None,
                stream=None) -> torch.Tensor:
     """Decode an NVFP4 KV cache of `shape` = (frames, tokens, heads, head_dim)
@@ -396,11 +425,28 @@ def dequantize(q: NVFP4Tensor, dtype=torch.float32, rows_per_domain: int = 0, ou
 
 
 def linear(x: torch.Tensor, w: NVFP4Tensor, out_dtype=torch.bfloat16, xq: NVFP4Tensor | None = None,
-           ws: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """W4A4 linear layer: quantize the activations, then the block-scaled GEMM
-    against pre-quantized weights w [N, K]."""
-    xq = quantize(x, axis=1, out=xq, ws=ws, stream=stream)
-    return gemm(xq, w, out_dtype=out_dtype, out=out, stream=stream)
+           ws: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None,
+           epilogue: int = EPI_NONE, amax_out: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A4 linear layer in one C call (nvfp4_linear): quantize the
+    activations x [M, K] into ``xq``, then the block-scaled GEMM against the
+    pre-quantized weights w [N, K] into ``out`` [M, N]."""
+    rows, cols = x.shape
+    if xq is None:
+        xq = NVFP4Tensor.empty(rows, cols, 1, x.device)
+    if out is None:
+        out = torch.empty((rows, w.rows), dtype=out_dtype, device=x.device)
+    elif tuple(out.shape) != (rows, w.rows):
+        raise ValueError(f"out must have shape {(rows, w.rows)}, got {tuple(out.shape)}")
+    if ws is None:
+        ws = _workspace(OP_QUANTIZE, rows, cols, x.device)
+    _need(ws, "ws")
+    if amax_out is not None:
+        _need(amax_out, "amax_out", dtype=torch.float32, min_numel=1)
+    cx, cw = xq.c(), w.c()
+    _check(_lib().nvfp4_linear(_ptr(x), _dtype_code(x), rows, cols, _ld(x), ctypes.byref(cw), ctypes.byref(cx),
+                               _ptr(out), _dtype_code(out), _ld(out), epilogue, _ptr(amax_out), _ptr(ws),
+                               ws.numel() * 4, _stream(stream)), "nvfp4_linear")
+    return out
 
 
 def ffn(x: torch.Tensor, w1: NVFP4Tensor, w2: NVFP4Tensor, out_dtype=torch.bfloat16, bufs: dict | None = None,

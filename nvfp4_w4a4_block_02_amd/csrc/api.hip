@@ -128,6 +128,8 @@ size_t nvfp4_workspace_bytes(int op, int64_t rows, int64_t cols) {
       return 0;
     case NVFP4_OP_KV_QUANT:
       return (size_t)mul_sat(ndomains(rows, cols), per_domain);
+    case NVFP4_OP_KV_QUANT_PAIR:
+      return (size_t)mul_sat(2, mul_sat(ndomains(rows, cols), per_domain));
     default:
       return 0;
   }
@@ -219,14 +221,22 @@ int nvfp4_quantize_noalloc(const void* x, int dtype, int64_t rows, int64_t cols,
   return quantize_impl(x, dtype, rows, cols, ld, axis, false, 0, out, ws, sizeof(scratch), stream);
 }
 
-static int gemm_impl(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int c_dtype, int64_t ldc,
-                     int epilogue, float* amax_out, int tile_fa, int tile_fb, void* stream) {
+// Host checks of a GEMM call (nothing launched).
+static int check_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, const void* c, int c_dtype, int64_t ldc,
+                      int epilogue, const float* amax_out) {
   if (!tensor_ok(a) || !tensor_ok(b) || !c || !valid_dtype(c_dtype)) return NVFP4_EINVAL;
   if (a->k != b->k || ldc < b->rows || !aligned16(c)) return NVFP4_EINVAL;
   if (epilogue != NVFP4_EPI_NONE && epilogue != NVFP4_EPI_GELU_TANH) return NVFP4_EINVAL;
   if (amax_out && ((uintptr_t)amax_out & 3u)) return NVFP4_EINVAL;
   if (a->rows >= ((int64_t)1 << 31) || b->rows >= ((int64_t)1 << 31) || a->k >= ((int64_t)1 << 31))
     return NVFP4_EUNSUPPORTED;
+  return NVFP4_OK;
+}
+
+static int gemm_impl(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int c_dtype, int64_t ldc,
+                     int epilogue, float* amax_out, int tile_fa, int tile_fb, void* stream) {
+  const int st = check_gemm(a, b, c, c_dtype, ldc, epilogue, amax_out);
+  if (st != NVFP4_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (a->rows == 0 || b->rows == 0) {
     return amax_out ? from_hip(nvfp4::launch_zero(amax_out, 1, s)) : NVFP4_OK;
@@ -246,6 +256,21 @@ int nvfp4_gemm_tiled(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int 
                      int epilogue, float* amax_out, int tile_fa, int tile_fb, void* stream) {
   if (!nvfp4::gemm_tiles_supported(tile_fa, tile_fb)) return NVFP4_EINVAL;
   return gemm_impl(a, b, c, c_dtype, ldc, epilogue, amax_out, tile_fa, tile_fb, stream);
+}
+
+int nvfp4_linear(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, const nvfp4_tensor* w,
+                 const nvfp4_tensor* xq, void* c, int c_dtype, int64_t ldc, int epilogue, float* amax_out,
+                 void* ws, size_t ws_bytes, void* stream) {
+  // Every check of both steps first, so that a bad argument launches nothing.
+  int st = check_dense_to_q(x, dtype, rows, cols, ld, 1, xq);
+  if (st != NVFP4_OK) return st;
+  if (!ws || !aligned16(ws)) return NVFP4_EINVAL;
+  if (ws_bytes < nvfp4_workspace_bytes(NVFP4_OP_QUANTIZE, rows, cols)) return NVFP4_EWORKSPACE;
+  st = check_gemm(xq, w, c, c_dtype, ldc, epilogue, amax_out);
+  if (st != NVFP4_OK) return st;
+  st = quantize_impl(x, dtype, rows, cols, ld, 1, false, 0, xq, ws, ws_bytes, stream);
+  if (st != NVFP4_OK) return st;
+  return gemm_impl(xq, w, c, c_dtype, ldc, epilogue, amax_out, 0, 0, stream);
 }
 
 static int kv_quant_impl(const void* kv, int64_t frames, int64_t tokens, int64_t heads, int64_t head_dim,
@@ -279,6 +304,28 @@ int nvfp4_kv_quant(const void* kv, int64_t frames, int64_t tokens, int64_t heads
 int nvfp4_kv_quant_4over6(const void* kv, int64_t frames, int64_t tokens, int64_t heads, int64_t head_dim,
                           int64_t frame_block, const nvfp4_tensor* out, void* ws, size_t ws_bytes, void* stream) {
   return kv_quant_impl(kv, frames, tokens, heads, head_dim, frame_block, out, ws, ws_bytes, stream, true);
+}
+
+int nvfp4_kv_quant_pair(const void* k, const void* v, int64_t frames, int64_t tokens, int64_t heads,
+                        int64_t head_dim, int64_t frame_block, int four_over_six, const nvfp4_tensor* k_out,
+                        const nvfp4_tensor* v_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!k || !v || !aligned16(k) || !aligned16(v) || frames < 0 || tokens < 0 || heads < 0 || head_dim < 0 ||
+      head_dim % 16 != 0 || frame_block <= 0 || (four_over_six != 0 && four_over_six != 1))
+    return NVFP4_EINVAL;
+  const int64_t rows = mul_sat(mul_sat(frames, tokens), heads);
+  if (rows == INT64_MAX || mul_sat(rows, head_dim / 16 + 1) >= kMaxBlocks) return NVFP4_EUNSUPPORTED;
+  if (!tensor_ok(k_out) || k_out->rows != rows || k_out->k != head_dim) return NVFP4_EINVAL;
+  if (!tensor_ok(v_out) || v_out->rows != rows || v_out->k != head_dim) return NVFP4_EINVAL;
+  if (!ws || !aligned16(ws)) return NVFP4_EINVAL;
+  if (ws_bytes < nvfp4_workspace_bytes(NVFP4_OP_KV_QUANT_PAIR, frames, frame_block)) return NVFP4_EWORKSPACE;
+  if (rows == 0 || head_dim == 0) return NVFP4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t rpd = (frame_block < frames ? frame_block : frames) * tokens * heads;  // <= rows
+  float* parts = static_cast<float*>(ws);
+  const nvfp4::DomGrid pg = nvfp4::amax_grid_rows(rows, head_dim, rpd);
+  if (nvfp4::launch_kv_pair_amax(k, v, rows, head_dim, rpd, parts, pg, s) != hipSuccess) return NVFP4_EHIP;
+  return from_hip(nvfp4::launch_kv_pair_encode(k, v, rows, head_dim, rpd, parts, pg, qout(k_out), qout(v_out),
+                                               four_over_six == 1, s));
 }
 
 int nvfp4_kv_dequant(const nvfp4_tensor* in, int64_t frames, int64_t tokens, int64_t heads, int64_t head_dim,

@@ -62,6 +62,17 @@ __device__ __forceinline__ float reduce_parts(const float* __restrict__ parts, i
   return workgroup_max(m);
 }
 
+// A second tensor of the same shape on the same launch (V beside K of one
+// KV cache): workgroups [wgs, 2 wgs) of the grid take it, its partial maxima
+// follow the first tensor's `parts` floats in the workspace, and it has its
+// own outputs.  Only the PAIR instances read it.
+struct Second {
+  const void* x;
+  QOut out;
+  uint32_t wgs;    // workgroups per tensor
+  uint32_t parts;  // partial maxima per tensor
+};
+
 // ---------------------------------------------------------------------------
 // Step 1, row layout: partial amax of each row domain.  Workgroup x of domain
 // d writes parts[d * grid.full + x] (grid.last partials for the last
@@ -71,13 +82,21 @@ __device__ __forceinline__ float reduce_parts(const float* __restrict__ parts, i
 // 256 MB Infinity Cache is then served from it (a 65 MB KV tensor: amax +
 // encode 33 -> 28 us; with non-temporal loads here the second read came
 // from HBM).
-template <int DT, bool RHT>
+template <int DT, bool RHT, bool PAIR = false>
 __global__ __launch_bounds__(kThreads) void amax_rows_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, int64_t rpd,
-    float* __restrict__ parts, uint32_t mask, DomGrid dg) {
+    float* __restrict__ parts, uint32_t mask, DomGrid dg, Second sec = {}) {
   constexpr int U = DT == 1 ? 4 : 2;
+  uint32_t g = blockIdx.x;
+  if constexpr (PAIR) {
+    if (g >= sec.wgs) {
+      g -= sec.wgs;
+      x = sec.x;
+      parts += sec.parts;
+    }
+  }
   uint32_t d, wx, nw;
-  dg.locate(blockIdx.x, d, wx, nw);
+  dg.locate(g, d, wx, nw);
   const int64_t r0 = (int64_t)d * rpd;
   const int64_t r1 = rows < r0 + rpd ? rows : r0 + rpd;
   const uint32_t bpr = (uint32_t)(cols / kBlock);
@@ -132,13 +151,24 @@ __global__ __launch_bounds__(kThreads) void amax_rows_kernel(
 // amax pass that
 // wrote `parts` (pdg.full partials per full domain, pdg.last for the last;
 // full = last = 1 for final amax values), `dg` the grid of this pass.
-template <int DT, bool RHT, bool FO6>
+template <int DT, bool RHT, bool FO6, bool PAIR = false>
 __global__ __launch_bounds__(kThreads) void encode_rows_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, int64_t rpd,
     const float* __restrict__ parts, DomGrid pdg, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, float* __restrict__ tscale, uint32_t mask, DomGrid dg) {
+    uint8_t* __restrict__ scales, float* __restrict__ tscale, uint32_t mask, DomGrid dg, Second sec = {}) {
+  uint32_t g = blockIdx.x;
+  if constexpr (PAIR) {
+    if (g >= sec.wgs) {
+      g -= sec.wgs;
+      x = sec.x;
+      parts += sec.parts;
+      codes = sec.out.codes;
+      scales = sec.out.scales;
+      tscale = sec.out.tscale;
+    }
+  }
   uint32_t d, wx, nw;
-  dg.locate(blockIdx.x, d, wx, nw);
+  dg.locate(g, d, wx, nw);
   const int64_t r0 = (int64_t)d * rpd;
   const int64_t r1 = rows < r0 + rpd ? rows : r0 + rpd;
   const uint32_t bpr = (uint32_t)(cols / kBlock);
@@ -625,6 +655,33 @@ hipError_t launch_encode_rows(const void* x, int dt, int64_t rows, int64_t cols,
     if (rht) NVFP4_ENC_ROWS(1, true, false); else NVFP4_ENC_ROWS(1, false, false);
   }
 #undef NVFP4_ENC_ROWS
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_pair_amax(const void* k, const void* v, int64_t rows, int64_t cols, int64_t rpd,
+                               float* parts, DomGrid pg, hipStream_t s) {
+  const unsigned n = total(pg);
+  const Second sec{v, QOut{}, n, n};
+  amax_rows_kernel<1, false, true><<<2 * n, kThreads, 0, s>>>(k, rows, cols, cols, rpd, parts, 0, pg, sec);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_pair_encode(const void* k, const void* v, int64_t rows, int64_t cols, int64_t rpd,
+                                 const float* parts, DomGrid pg, QOut k_out, QOut v_out, bool four_over_six,
+                                 hipStream_t s) {
+  int64_t nd, last;
+  domains(rows, rpd, nd, last);
+  // workgroups per domain as for one tensor, but the cap on the launch's
+  // total (encode_count) spread over the domains of both tensors
+  const DomGrid eg{encode_count(rpd * (cols / kBlock), 2 * nd), encode_count(last * (cols / kBlock), 2 * nd),
+                   (uint32_t)nd};
+  const Second sec{v, v_out, total(eg), total(pg)};
+#define NVFP4_ENC_PAIR(F)                                                                                  \
+  encode_rows_kernel<1, false, F, true><<<2 * total(eg), kThreads, 0, s>>>(k, rows, cols, cols, rpd, parts, \
+                                                                        pg, k_out.codes, k_out.scales,      \
+                                                                        k_out.tscale, 0, eg, sec)
+  if (four_over_six) NVFP4_ENC_PAIR(true); else NVFP4_ENC_PAIR(false);
+#undef NVFP4_ENC_PAIR
   return hipGetLastError();
 }
 

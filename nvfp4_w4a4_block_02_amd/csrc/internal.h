@@ -64,6 +64,16 @@ hipError_t launch_encode_cols(const void* x, int dt, int64_t rows, int64_t cols,
                               const float* parts, DomGrid pg, QOut out, bool rht, uint32_t mask,
                               hipStream_t s, int64_t out_k = 0);
 
+// K and V of one cache (bf16, contiguous, same shape) on one launch per
+// pass: the amax pass writes each tensor's partial maxima as the one-tensor
+// pass would, K's at parts[0, total(pg)) and V's right after them; the
+// encode pass reads them back from there.
+hipError_t launch_kv_pair_amax(const void* k, const void* v, int64_t rows, int64_t cols, int64_t rows_per_domain,
+                               float* parts, DomGrid pg, hipStream_t s);
+hipError_t launch_kv_pair_encode(const void* k, const void* v, int64_t rows, int64_t cols,
+                                 int64_t rows_per_domain, const float* parts, DomGrid pg, QOut k_out,
+                                 QOut v_out, bool four_over_six, hipStream_t s);
+
 // Step 7.
 hipError_t launch_dequant(QOut in, int64_t rows, int64_t k, int64_t rows_per_domain, void* out,
                           int out_dt, hipStream_t s);

@@ -144,6 +144,40 @@ def test_gemm_rejects_bad_arguments(nv):
     assert gt(ctypes.byref(_t(nv, 0, 64)), ctypes.byref(b), c, 0, 16, 0, None, 4, 4, _stream()) == 0
 
 
+def test_linear_rejects_bad_arguments_of_either_step(nv):
+    """nvfp4_linear checks the quantize's and the GEMM's arguments before it
+    launches anything: a bad GEMM argument is refused even though the
+    quantize's are good (every call here would otherwise launch on memory
+    that does not exist)."""
+    lin = nv.lib.nvfp4_linear
+    x, c, ws = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE)
+    xq, w = _t(nv, 8, 64), _t(nv, 16, 64)
+    EINVAL, EWS = -1, -3
+
+    def call(x=x, dt=1, rows=8, cols=64, ld=64, w=w, xq=xq, c=c, cdt=0, ldc=16, epi=0, amax=None, ws=ws,
+             wsb=4096):
+        return lin(x, dt, rows, cols, ld, ctypes.byref(w), ctypes.byref(xq), c, cdt, ldc, epi, amax, ws, wsb,
+                   _stream())
+
+    # quantize side
+    assert call(x=None) == EINVAL
+    assert call(dt=5) == EINVAL
+    assert call(ld=32) == EINVAL
+    assert call(xq=_t(nv, 9, 64)) == EINVAL        # xq rows != rows
+    assert call(ws=None) == EINVAL
+    assert call(wsb=8) == EWS
+    # GEMM side, with a good quantize
+    assert call(w=_t(nv, 16, 48)) == EINVAL        # K mismatch
+    assert call(ldc=8) == EINVAL                   # ldc < N
+    assert call(cdt=3) == EINVAL
+    assert call(epi=9) == EINVAL
+    assert call(c=None) == EINVAL
+    assert call(amax=ctypes.c_void_p(FAKE + 2)) == EINVAL
+    assert call(w=_t(nv, 16, 64, codes=FAKE + 1)) == EINVAL
+    # zero rows: nothing to do (no amax_out to clear)
+    assert call(rows=0, xq=_t(nv, 0, 64)) == 0
+
+
 @pytest.mark.parametrize("entry", ["nvfp4_kv_quant", "nvfp4_kv_quant_4over6"])
 def test_kv_rejects_bad_arguments(nv, entry):
     kq = getattr(nv.lib, entry)
@@ -161,6 +195,28 @@ def test_kv_rejects_bad_arguments(nv, entry):
     assert kd(ctypes.byref(out), 12, 4, 2, 32, 8, None, _stream()) == -1
     assert kd(ctypes.byref(out), 12, 4, 2, 32, 8, ctypes.c_void_p(FAKE + 8), _stream()) == -1
     assert kd(ctypes.byref(_t(nv, 96, 16)), 12, 4, 2, 32, 8, ctypes.c_void_p(FAKE), _stream()) == -1
+
+
+def test_kv_quant_pair_rejects_bad_arguments(nv):
+    kq = nv.lib.nvfp4_kv_quant_pair
+    ko, vo = _t(nv, 12 * 4 * 2, 32), _t(nv, 12 * 4 * 2, 32)
+    ws = ctypes.c_void_p(FAKE)
+    x = ctypes.c_void_p(FAKE)
+
+    def call(k=x, v=x, f=12, fb=8, fo6=0, ko=ko, vo=vo, ws=ws, wsb=16384):
+        return kq(k, v, f, 4, 2, 32, fb, fo6, ctypes.byref(ko), ctypes.byref(vo), ws, wsb, _stream())
+
+    assert nv.workspace_bytes(nv.OP_KV_QUANT_PAIR, 12, 8) == 16384  # two tensors x two frame blocks
+    assert call(k=None) == -1
+    assert call(v=ctypes.c_void_p(FAKE + 4)) == -1
+    assert call(fb=0) == -1
+    assert call(fo6=2) == -1
+    assert call(ko=_t(nv, 95, 32)) == -1
+    assert call(vo=_t(nv, 96, 16)) == -1
+    assert call(vo=_t(nv, 96, 32, tscale=0)) == -1
+    assert call(ws=None) == -1
+    assert call(wsb=8192) == -3  # one tensor's workspace is not enough
+    assert call(f=0, ko=_t(nv, 0, 32), vo=_t(nv, 0, 32)) == 0
 
 
 def test_amax_encode_dequant_reject_bad_arguments(nv):

@@ -314,30 +314,50 @@ def test_full_attn_proj_operands(nv):
     assert_q_exact(gw, oracle.quantize(d["w"]), "W")
 
 
-def test_full_kv_codec(nv):
+@pytest.mark.parametrize("shape,fb", [((12, 5, 3, 32), 8), ((9, 7, 2, 128), 4), ((3, 11, 4, 64), 8),
+                                      ((17, 2, 1, 16), 5), ((4, 40, 3, 128), 1)])
+@pytest.mark.parametrize("fo6", [False, True])
+def test_kv_quant_pair_small(nv, shape, fb, fo6):
+    """K and V through nvfp4_kv_quant_pair (one amax and one encode launch for
+    both) against the oracle: frame blocks with a partial last block, one
+    block over the whole window (fb 8 > 3 frames), one frame per block."""
+    f, t, h, d = shape
+    log(f"kv quant pair {shape} frame_block {fb} four_over_six {fo6}")
+    kv = workloads.kv_cache(frames=f, tokens=t, heads=h, head_dim=d, seed=140 + f)
+    gk, gv = nv.kv_quant_pair(dev_bf16(kv["k"]), dev_bf16(kv["v"]), frame_block=fb, four_over_six=fo6)
+    ref = oracle.kv_quantize_4over6 if fo6 else oracle.kv_quantize
+    ok, ov = ref(widen(kv["k"]), frame_block=fb), ref(widen(kv["v"]), frame_block=fb)
+    torch.cuda.synchronize()
+    assert_q_exact(gk, ok, f"pair K {shape}")
+    assert_q_exact(gv, ov, f"pair V {shape}")
+
+
+def _full_kv(nv, fo6):
     d = workloads.kv_cache()
     shape = (12, 880, 24, 128)
+    ref = oracle.kv_quantize_4over6 if fo6 else oracle.kv_quantize
+    oq = {name: ref(widen(d[name]).reshape(shape)) for name in ("k", "v")}
     for name in ("k", "v"):
-        log(f"full-size KV codec {name} {shape}")
-        gq = nv.kv_quant(dev_bf16(d[name]))
-        oq = oracle.kv_quantize(widen(d[name]).reshape(shape))
+        log(f"full-size KV codec {name} {shape} four_over_six {fo6}")
+        gq = nv.kv_quant(dev_bf16(d[name]), four_over_six=fo6)
         torch.cuda.synchronize()
-        assert_q_exact(gq, oq, f"kv {name}")
+        assert_q_exact(gq, oq[name], f"kv {name}")
         y = host_bf16_bits(nv.kv_dequant(gq, shape))
-        assert np.array_equal(y, oracle.kv_dequantize(oq, *shape))
+        assert np.array_equal(y, oracle.kv_dequantize(oq[name], *shape))
+    # the pair entry point, as the bench times it
+    log(f"full-size KV codec, K and V in one call, four_over_six {fo6}")
+    gk, gv = nv.kv_quant_pair(dev_bf16(d["k"]), dev_bf16(d["v"]), four_over_six=fo6)
+    torch.cuda.synchronize()
+    assert_q_exact(gk, oq["k"], "pair K")
+    assert_q_exact(gv, oq["v"], "pair V")
+
+
+def test_full_kv_codec(nv):
+    _full_kv(nv, False)
 
 
 def test_full_kv_codec_four_over_six(nv):
-    d = workloads.kv_cache()
-    shape = (12, 880, 24, 128)
-    for name in ("k", "v"):
-        log(f"full-size KV codec, Four Over Six, {name} {shape}")
-        gq = nv.kv_quant(dev_bf16(d[name]), four_over_six=True)
-        oq = oracle.kv_quantize_4over6(widen(d[name]).reshape(shape))
-        torch.cuda.synchronize()
-        assert_q_exact(gq, oq, f"kv 4/6 {name}")
-        y = host_bf16_bits(nv.kv_dequant(gq, shape))
-        assert np.array_equal(y, oracle.kv_dequantize(oq, *shape))
+    _full_kv(nv, True)
 
 
 def test_full_rht_gradient(nv):

@@ -250,6 +250,39 @@ def test_tiny_linear_full(nv):
     c = nv.gemm(ga, gb, out_dtype=torch.float32).cpu().numpy()
     cref, bound = oracle.gemm_ref(oa, ob)
     assert_gemm_close(c, cref, bound, False, "workload 1")
+    # the one-call linear layer leaves the same activation codes and output
+    xq = nv.NVFP4Tensor.empty(256, 512, 1, "cuda")
+    c1 = nv.linear(dev_f32(d["a"]), gb, out_dtype=torch.float32, xq=xq).cpu().numpy()
+    assert_q_exact(xq, oa, "A (nvfp4_linear)")
+    assert np.array_equal(c1.view(np.uint32), c.view(np.uint32))
+
+
+@pytest.mark.parametrize("m,n,k,xdt,odt,epi", [(17, 33, 48, "bf16", "f32", 0), (255, 130, 512, "f32", "bf16", 1),
+                                                (129, 257, 384, "bf16", "bf16", 1), (300, 520, 1024, "f32", "f32", 1)])
+def test_linear_equals_quantize_then_gemm(nv, m, n, k, xdt, odt, epi):
+    """nvfp4_linear (one call) gives bit for bit the codes, output and
+    output amax of nvfp4_quantize followed by nvfp4_gemm; the second call
+    reuses the same buffers, so stale contents would show."""
+    log(f"linear {m}x{n}x{k} x {xdt} -> {odt} epilogue {epi}")
+    rng = np.random.default_rng(m + 7 * n + 11 * k)
+    x = (rng.standard_normal((m, k)) * 3).astype(np.float32)
+    gx = dev_f32(x) if xdt == "f32" else dev_f32(x).to(torch.bfloat16)
+    gw = nv.quantize(dev_f32((rng.standard_normal((n, k)) * 0.05).astype(np.float32)))
+    dt = torch.float32 if odt == "f32" else torch.bfloat16
+    want_q = nv.quantize(gx)
+    want_amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    want = nv.gemm(want_q, gw, out_dtype=dt, epilogue=epi, amax_out=want_amax)
+    xq = nv.NVFP4Tensor.empty(m, k, 1, "cuda")
+    out = torch.empty((m, n), dtype=dt, device="cuda")
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        nv.linear(gx, gw, xq=xq, out=out, epilogue=epi, amax_out=amax)
+        torch.cuda.synchronize()
+        assert torch.equal(xq.codes, want_q.codes) and torch.equal(xq.scales, want_q.scales)
+        assert torch.equal(xq.tscale, want_q.tscale)
+        assert torch.equal(out.view(torch.int16 if odt == "bf16" else torch.int32),
+                           want.view(torch.int16 if odt == "bf16" else torch.int32))
+        assert torch.equal(amax, want_amax)
 
 
 def test_attn_proj_full(nv):
