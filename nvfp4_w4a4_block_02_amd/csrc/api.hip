@@ -195,7 +195,8 @@ static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, i
     e = nvfp4::launch_amax_parts_cols(x, dtype, rows, cols, ld, parts, pg, rht, mask, s);
   }
   if (e != hipSuccess) return NVFP4_EHIP;
-  if (axis == 1) e = nvfp4::launch_encode_rows(x, dtype, rows, cols, ld, 0, parts, pg, qout(out), rht, mask, s);
+  if (axis == 1)
+    e = nvfp4::launch_encode_rows(x, dtype, rows, cols, ld, 0, parts, pg, qout(out), rht, mask, s, false, true);
   else e = nvfp4::launch_encode_cols(x, dtype, rows, cols, ld, parts, pg, qout(out), rht, mask, s, out->k);
   return from_hip(e);
 }
@@ -293,7 +294,7 @@ static int kv_quant_impl(const void* kv, int64_t frames, int64_t tokens, int64_t
       hipSuccess)
     return NVFP4_EHIP;
   return from_hip(nvfp4::launch_encode_rows(kv, NVFP4_BF16, rows, head_dim, head_dim, rpd, parts, pg,
-                                            qout(out), false, 0, s, four_over_six));
+                                            qout(out), false, 0, s, four_over_six, true));
 }
 
 int nvfp4_kv_quant(const void* kv, int64_t frames, int64_t tokens, int64_t heads, int64_t head_dim,

@@ -56,9 +56,12 @@ hipError_t launch_reduce_parts(const float* parts, DomGrid pg, float* amax, hipS
 
 // Steps 2-6 from per-domain partial maxima laid out as `pg` says.
 // four_over_six: Four Over Six block-scale selection (not combined with rht).
+// pg_is_amax_grid: `pg` is the grid of the amax pass that just read this
+// same tensor (not final per-domain values), which the encode may reuse.
 hipError_t launch_encode_rows(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
                               int64_t rows_per_domain, const float* parts, DomGrid pg, QOut out,
-                              bool rht, uint32_t mask, hipStream_t s, bool four_over_six = false);
+                              bool rht, uint32_t mask, hipStream_t s, bool four_over_six = false,
+                              bool pg_is_amax_grid = false);
 // out_k: length of the output rows (>= rows; blocks past rows are zeroed).
 hipError_t launch_encode_cols(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld,
                               const float* parts, DomGrid pg, QOut out, bool rht, uint32_t mask,
