@@ -384,7 +384,10 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs, only, settle_ms):
             nv.kv_quant(s["k"], out=s["kq"], ws=s["ws"], stream=stream, four_over_six=fo6)
             nv.kv_quant(s["v"], out=s["vq"], ws=s["ws"], stream=stream, four_over_six=fo6)
 
-        def kvd(s):
+        def kvd(s):  # K and V in one launch (nvfp4_kv_dequant_pair)
+            nv.kv_dequant_pair(s["kq"], s["vq"], shape, k_out=s["ko"], v_out=s["vo"], stream=stream)
+
+        def kvd_two(s):
             nv.kv_dequant(s["kq"], shape, out=s["ko"], stream=stream)
             nv.kv_dequant(s["vq"], shape, out=s["vo"], stream=stream)
 
@@ -397,6 +400,7 @@ def bench_rows(nv, torch, wl, steps, warmup, copy_gbs, only, settle_ms):
         if want("kv_dequant"):
             kvq(kvsets[0]), kvq(kvsets[1]), kvq(kvsets[2]), kvq(kvsets[3])
             out["kv_dequant"] = hbm_row(timed(kvd, kvsets, steps, warmup), kv_bytes)
+            out["kv_dequant"]["ms_two_calls"] = timed(kvd_two, kvsets, steps, warmup)["ms"]
         del kvsets
     # Window attention reading the NVFP4 KV cache directly: the chunk's 3
     # latent frames of queries against the 12-frame cache (frame-causal).

@@ -303,6 +303,16 @@ int nvfp4_kv_dequant(const nvfp4_tensor *in, int64_t frames, int64_t tokens, int
                      int64_t head_dim, int64_t frame_block, void *out, void *stream);
 
 /*
+ * K and V of one cache decoded in one launch (the pages' dequant of the
+ * NVFP4 KV window: hyper.ai summary, section "方法"): the same bf16 values as
+ * nvfp4_kv_dequant on k_in into k_out and on v_in into v_out.  Both inputs
+ * describe [frames][tokens][heads][head_dim] with the same frame_block.
+ */
+int nvfp4_kv_dequant_pair(const nvfp4_tensor *k_in, const nvfp4_tensor *v_in, int64_t frames,
+                          int64_t tokens, int64_t heads, int64_t head_dim, int64_t frame_block,
+                          void *k_out, void *v_out, void *stream);
+
+/*
  * Frame-causal window attention that reads the NVFP4 KV cache directly (the
  * consumer of the cache: 9 local latent frames plus 3 sink frames kept in the
  * cache, 171host.com "LongLive 2.0 技术拆解", section 2.2; NVFP4 cache in

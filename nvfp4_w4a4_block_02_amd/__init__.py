@@ -65,6 +65,7 @@ def _load():
         "nvfp4_kv_quant_4over6": (I, [P, I64, I64, I64, I64, I64, TP, P, SZ, P]),
         "nvfp4_kv_quant_pair": (I, [P, P, I64, I64, I64, I64, I64, I, TP, TP, P, SZ, P]),
         "nvfp4_kv_dequant": (I, [TP, I64, I64, I64, I64, I64, P, P]),
+        "nvfp4_kv_dequant_pair": (I, [TP, TP, I64, I64, I64, I64, I64, P, P, P]),
         "nvfp4_dequantize": (I, [TP, I64, P, I, P]),
         "nvfp4_kv_attention": (I, [P, I64, TP, TP, I64, I64, I64, I64, I64, P, I, P]),
     }
@@ -93,7 +94,7 @@ def __getattr__(name):  # module attribute `lib` loads the library on first acce
 
 EXPORTED = ("nvfp4_version", "nvfp4_status_string", "nvfp4_workspace_bytes", "nvfp4_amax",
             "nvfp4_encode", "nvfp4_quantize", "nvfp4_quantize_noalloc", "rht16_quantize", "nvfp4_gemm", "nvfp4_gemm_tiled", "nvfp4_linear", "nvfp4_kv_quant",
-            "nvfp4_kv_quant_4over6", "nvfp4_kv_quant_pair", "nvfp4_kv_dequant", "nvfp4_dequantize", "nvfp4_kv_attention")
+            "nvfp4_kv_quant_4over6", "nvfp4_kv_quant_pair", "nvfp4_kv_dequant", "nvfp4_kv_dequant_pair", "nvfp4_dequantize", "nvfp4_kv_attention")
 
 
 def _check(status: int, what: str):
@@ -387,6 +388,24 @@ def kv_dequant(q: NVFP4Tensor, shape, frame_block: int = 8, out: torch.Tensor | 
     _check(_lib().nvfp4_kv_dequant(ctypes.byref(ct), f, t, h, d, frame_block, _ptr(out), _stream(stream)),
            "nvfp4_kv_dequant")
     return out
+
+
+def kv_dequant_pair(kq: NVFP4Tensor, vq: NVFP4Tensor, shape, frame_block: int = 8,
+                    k_out: torch.Tensor | None = None, v_out: torch.Tensor | None = None,
+                    stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """K and V of one cache decoded to bf16 in one launch (nvfp4_kv_dequant_pair)."""
+    f, t, h, d = shape
+    outs = []
+    for o in (k_out, v_out):
+        if o is None:
+            o = torch.empty((f, t, h, d), dtype=torch.bfloat16, device=kq.codes.device)
+        _need(o, "out", shape=(f, t, h, d), dtype=torch.bfloat16)
+        outs.append(o)
+    nd = -(-f // frame_block) if frame_block > 0 else 1
+    ck, cv = kq.c(nd), vq.c(nd)
+    _check(_lib().nvfp4_kv_dequant_pair(ctypes.byref(ck), ctypes.byref(cv), f, t, h, d, frame_block, _ptr(outs[0]),
+                                        _ptr(outs[1]), _stream(stream)), "nvfp4_kv_dequant_pair")
+    return outs[0], outs[1]
 
 
 def kv_attention(q: torch.Tensor, k: NVFP4Tensor, v: NVFP4Tensor, shape, frame_block: int = 8,

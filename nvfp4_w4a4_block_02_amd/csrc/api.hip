@@ -341,6 +341,21 @@ int nvfp4_kv_dequant(const nvfp4_tensor* in, int64_t frames, int64_t tokens, int
   return from_hip(nvfp4::launch_dequant(qout(in), rows, head_dim, rpd, out, NVFP4_BF16, (hipStream_t)stream));
 }
 
+int nvfp4_kv_dequant_pair(const nvfp4_tensor* k_in, const nvfp4_tensor* v_in, int64_t frames, int64_t tokens,
+                          int64_t heads, int64_t head_dim, int64_t frame_block, void* k_out, void* v_out,
+                          void* stream) {
+  if (!tensor_ok(k_in) || !tensor_ok(v_in) || !k_out || !v_out || !aligned16(k_out) || !aligned16(v_out) ||
+      frames < 0 || tokens < 0 || heads < 0 || frame_block <= 0)
+    return NVFP4_EINVAL;
+  const int64_t rows = mul_sat(mul_sat(frames, tokens), heads);
+  if (rows == INT64_MAX || mul_sat(rows, head_dim / 16 + 1) >= kMaxBlocks) return NVFP4_EUNSUPPORTED;
+  if (k_in->rows != rows || k_in->k != head_dim || v_in->rows != rows || v_in->k != head_dim) return NVFP4_EINVAL;
+  if (rows == 0 || head_dim == 0) return NVFP4_OK;
+  const int64_t rpd = (frame_block < frames ? frame_block : frames) * tokens * heads;  // <= rows
+  return from_hip(nvfp4::launch_kv_pair_dequant(qout(k_in), qout(v_in), rows, head_dim, rpd, k_out, v_out,
+                                                (hipStream_t)stream));
+}
+
 int nvfp4_kv_attention(const void* q, int64_t q_frames, const nvfp4_tensor* k, const nvfp4_tensor* v,
                        int64_t frames, int64_t tokens, int64_t heads, int64_t head_dim, int64_t frame_block,
                        void* out, int out_dtype, void* stream) {

@@ -478,16 +478,30 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(
 // float32 (one code half-word) — so that consecutive lanes store consecutive
 // 16 bytes (one contiguous 1 KiB per wavefront store) and load consecutive
 // code bytes.  Four units are in flight per thread.
-template <int OUT>
+// PAIR: a second tensor of the same shape (V beside K) on the same launch:
+// the second half of the grid decodes `second` into out2.
+template <int OUT, bool PAIR = false>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const float* __restrict__ ts, int64_t rows, int64_t k, int64_t rpd, void* __restrict__ out) {
+    const float* __restrict__ ts, int64_t rows, int64_t k, int64_t rpd, void* __restrict__ out,
+    QOut second = {}, void* __restrict__ out2 = nullptr) {
   constexpr int E = OUT == 1 ? 8 : 4;                  // elements per unit
   const uint64_t nunits = (uint64_t)rows * (uint64_t)k / E;
   const uint64_t upd = (uint64_t)(rpd < rows ? rpd : rows) * (uint64_t)k / E;  // units per domain
   const bool one_domain = (rpd >= rows);
   const bool narrow = nunits <= 0xFFFFFFFFull;  // 32-bit domain division suffices
-  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  uint32_t wg = blockIdx.x, nwg = gridDim.x;
+  if constexpr (PAIR) {
+    nwg /= 2;
+    if (wg >= nwg) {
+      wg -= nwg;
+      codes = second.codes;
+      scales = second.scales;
+      ts = second.tscale;
+      out = out2;
+    }
+  }
+  const uint64_t stride = (uint64_t)nwg * kThreads;
   // Tensor scale of unit u's domain.  A thread's units rise monotonically and
   // a domain spans millions of units, so the division runs only when u
   // leaves the cached range.
@@ -527,7 +541,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
                                   reinterpret_cast<float4_t*>(out) + u);
     }
   };
-  uint64_t u = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+  uint64_t u = (uint64_t)wg * kThreads + threadIdx.x;
   for (; u + 3 * stride < nunits; u += 4 * stride) {
     // the four units' loads first, then their arithmetic and stores
     uint32_t w[4], sb[4];
@@ -710,6 +724,17 @@ hipError_t launch_encode_cols(const void* x, int dt, int64_t rows, int64_t cols,
   if (dt == 0) { if (rht) NVFP4_ENC_COLS(0, true); else NVFP4_ENC_COLS(0, false); }
   else { if (rht) NVFP4_ENC_COLS(1, true); else NVFP4_ENC_COLS(1, false); }
 #undef NVFP4_ENC_COLS
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_pair_dequant(QOut k_in, QOut v_in, int64_t rows, int64_t k, int64_t rpd, void* k_out,
+                                 void* v_out, hipStream_t s) {
+  if (rpd <= 0 || rpd > rows) rpd = rows;
+  const int64_t units = rows * k / 8;
+  int64_t g = (units + 4 * kThreads - 1) / (4 * kThreads);
+  const unsigned grid = (unsigned)(g < 4096 ? (g < 1 ? 1 : g) : 4096);  // per tensor, as one tensor's launch
+  dequant_kernel<1, true><<<2 * grid, kThreads, 0, s>>>(k_in.codes, k_in.scales, k_in.tscale, rows, k, rpd, k_out,
+                                                        v_in, v_out);
   return hipGetLastError();
 }
 

@@ -77,6 +77,10 @@ hipError_t launch_kv_pair_encode(const void* k, const void* v, int64_t rows, int
                                  int64_t rows_per_domain, const float* parts, DomGrid pg, QOut k_out,
                                  QOut v_out, bool four_over_six, hipStream_t s);
 
+// Step 7 for K and V of one cache (same shape) on one launch, bf16 out.
+hipError_t launch_kv_pair_dequant(QOut k_in, QOut v_in, int64_t rows, int64_t k, int64_t rows_per_domain,
+                                  void* k_out, void* v_out, hipStream_t s);
+
 // Step 7.
 hipError_t launch_dequant(QOut in, int64_t rows, int64_t k, int64_t rows_per_domain, void* out,
                           int out_dt, hipStream_t s);

@@ -217,6 +217,13 @@ def test_kv_quant_pair_rejects_bad_arguments(nv):
     assert call(ws=None) == -1
     assert call(wsb=8192) == -3  # one tensor's workspace is not enough
     assert call(f=0, ko=_t(nv, 0, 32), vo=_t(nv, 0, 32)) == 0
+    kd = nv.lib.nvfp4_kv_dequant_pair
+    o = ctypes.c_void_p(FAKE)
+    assert kd(ctypes.byref(ko), ctypes.byref(vo), 12, 4, 2, 32, 8, o, None, _stream()) == -1
+    assert kd(ctypes.byref(ko), ctypes.byref(vo), 12, 4, 2, 32, 8, ctypes.c_void_p(FAKE + 8), o, _stream()) == -1
+    assert kd(ctypes.byref(ko), ctypes.byref(_t(nv, 96, 16)), 12, 4, 2, 32, 8, o, o, _stream()) == -1
+    assert kd(ctypes.byref(ko), ctypes.byref(vo), 12, 4, 2, 32, 0, o, o, _stream()) == -1
+    assert kd(ctypes.byref(_t(nv, 0, 32)), ctypes.byref(_t(nv, 0, 32)), 0, 4, 2, 32, 8, o, o, _stream()) == 0
 
 
 def test_amax_encode_dequant_reject_bad_arguments(nv):

@@ -330,6 +330,9 @@ def test_kv_quant_pair_small(nv, shape, fb, fo6):
     torch.cuda.synchronize()
     assert_q_exact(gk, ok, f"pair K {shape}")
     assert_q_exact(gv, ov, f"pair V {shape}")
+    yk, yv = nv.kv_dequant_pair(gk, gv, shape, frame_block=fb)
+    assert np.array_equal(host_bf16_bits(yk), oracle.kv_dequantize(ok, f, t, h, d, frame_block=fb))
+    assert np.array_equal(host_bf16_bits(yv), oracle.kv_dequantize(ov, f, t, h, d, frame_block=fb))
 
 
 def _full_kv(nv, fo6):
@@ -350,6 +353,9 @@ def _full_kv(nv, fo6):
     torch.cuda.synchronize()
     assert_q_exact(gk, oq["k"], "pair K")
     assert_q_exact(gv, oq["v"], "pair V")
+    yk, yv = nv.kv_dequant_pair(gk, gv, shape)
+    assert np.array_equal(host_bf16_bits(yk), oracle.kv_dequantize(oq["k"], *shape))
+    assert np.array_equal(host_bf16_bits(yv), oracle.kv_dequantize(oq["v"], *shape))
 
 
 def test_full_kv_codec(nv):
