@@ -284,7 +284,8 @@ int nvfp4_kv_quant_4over6(const void *kv, int64_t frames, int64_t tokens, int64_
  * nvfp4_kv_quant_4over6 (four_over_six = 1) called on k into k_out and on v
  * into v_out, with the amax pass of both tensors in one launch and the encode
  * pass of both in another (two launches instead of four).  k and v: device
- * bf16 [frames][tokens][heads][head_dim], contiguous, same shape.
+ * bf16 [frames][tokens][heads][head_dim], contiguous, same shape; k_out and
+ * v_out must not overlap.
  * ws: >= nvfp4_workspace_bytes(NVFP4_OP_KV_QUANT_PAIR, frames, frame_block)
  * (twice the one-tensor workspace).  Other values of four_over_six return
  * NVFP4_EINVAL; errors otherwise as nvfp4_kv_quant.
