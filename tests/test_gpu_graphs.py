@@ -97,3 +97,58 @@ def test_ffn_graph_replays_match_eager(nv):
         assert torch.equal(got_hmax.view(torch.int32), ref["hmax"].view(torch.int32)), rep
         assert _q_equal(got_hq, ref["hq"]), rep
         assert torch.equal(got_y.view(torch.int16), ref_y.view(torch.int16)), rep
+
+
+def test_one_call_linear_and_kv_pair_graph_replays_match_eager(nv):
+    """nvfp4_linear (as the bench's graph figure captures it) and the K+V
+    pair quantize + dequantize captured once and replayed on three inputs;
+    every replay equals eager calls of the same entry points bit for bit."""
+    m, n, k = 256, 512, 512
+    shape = (3, 40, 4, 64)
+    log(f"graph replay: nvfp4_linear {m}x{n}x{k}, K+V pair codec {shape}")
+    d = workloads.tiny_linear(m=m, n=n, k=k)
+    wq = nv.quantize(torch.from_numpy(d["w"]).cuda())
+    a = torch.empty((m, k), dtype=torch.float32, device="cuda")
+    aq = nv.NVFP4Tensor.empty(m, k, 1, "cuda")
+    ws = nv._workspace(nv.OP_QUANTIZE, m, k, "cuda")
+    c = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    kk = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    vv = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    rows = shape[0] * shape[1] * shape[2]
+    kq, vq = nv.NVFP4Tensor.empty(rows, shape[3], 1, "cuda"), nv.NVFP4Tensor.empty(rows, shape[3], 1, "cuda")
+    kws = nv._workspace(nv.OP_KV_QUANT_PAIR, shape[0], 8, "cuda")
+    ko = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    vo = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+
+    def calls():
+        nv.linear(a, wq, xq=aq, ws=ws, out=c)
+        nv.kv_quant_pair(kk, vv, k_out=kq, v_out=vq, ws=kws)
+        nv.kv_dequant_pair(kq, vq, shape, k_out=ko, v_out=vo)
+
+    rng = np.random.default_rng(11)
+    a.copy_(torch.from_numpy(d["a"]))
+    kk.normal_()
+    vv.normal_()
+    calls()                               # warm up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(3):
+        a.copy_(torch.from_numpy((rng.standard_normal((m, k)) * (1.0 + 10.0 * rep)).astype(np.float32)))
+        kk.copy_(torch.from_numpy((rng.standard_normal(shape) * (0.5 + rep)).astype(np.float32)).to(torch.bfloat16))
+        vv.copy_(torch.from_numpy((rng.standard_normal(shape) * 3.0).astype(np.float32)).to(torch.bfloat16))
+        g.replay()
+        torch.cuda.synchronize()
+        got = [c.clone(), ko.clone(), vo.clone()]
+        got_q = [nv.NVFP4Tensor(t.codes.clone(), t.scales.clone(), t.tscale.clone()) for t in (aq, kq, vq)]
+        ref_c = nv.linear(a, wq, out_dtype=torch.float32)
+        ref_k, ref_v = nv.kv_quant_pair(kk, vv)
+        ref_ko, ref_vo = nv.kv_dequant_pair(ref_k, ref_v, shape)
+        ref_a = nv.quantize(a)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0].view(torch.int32), ref_c.view(torch.int32)), f"replay {rep}: linear output"
+        assert torch.equal(got[1].view(torch.int16), ref_ko.view(torch.int16)), f"replay {rep}: K dequant"
+        assert torch.equal(got[2].view(torch.int16), ref_vo.view(torch.int16)), f"replay {rep}: V dequant"
+        for gq, rq, nm in zip(got_q, (ref_a, ref_k, ref_v), ("A", "K", "V")):
+            assert _q_equal(gq, rq), f"replay {rep}: {nm} codes"
