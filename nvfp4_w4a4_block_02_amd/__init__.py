@@ -448,23 +448,42 @@ def linear(x: torch.Tensor, w: NVFP4Tensor, out_dtype=torch.bfloat16, xq: NVFP4T
            epilogue: int = EPI_NONE, amax_out: torch.Tensor | None = None) -> torch.Tensor:
     """W4A4 linear layer in one C call (nvfp4_linear): quantize the
     activations x [M, K] into ``xq``, then the block-scaled GEMM against the
-    pre-quantized weights w [N, K] into ``out`` [M, N]."""
+    pre-quantized weights w [N, K] into ``out`` [M, N].
+
+    This is the latency path of small layers, so its checks are the ones the
+    C ABI cannot make from raw pointers, written out inline: every tensor on
+    the GPU, rows of x and out contiguous, out of shape [M, N], a contiguous
+    workspace (its byte count goes to the C side, which checks it, the
+    dtypes, alignment and sizes)."""
     rows, cols = x.shape
     if xq is None:
         xq = NVFP4Tensor.empty(rows, cols, 1, x.device)
     if out is None:
         out = torch.empty((rows, w.rows), dtype=out_dtype, device=x.device)
-    elif tuple(out.shape) != (rows, w.rows):
-        raise ValueError(f"out must have shape {(rows, w.rows)}, got {tuple(out.shape)}")
     if ws is None:
         ws = _workspace(OP_QUANTIZE, rows, cols, x.device)
-    _need(ws, "ws")
+    osh = out.shape
+    if len(osh) != 2 or osh[0] != rows or osh[1] != w.codes.shape[0]:
+        raise ValueError(f"out must have shape {(rows, w.rows)}, got {tuple(osh)}")
+    if not (x.is_cuda and out.is_cuda and ws.is_cuda):
+        raise TypeError("x, out and ws must be CUDA tensors")
+    if not ws.is_contiguous():
+        raise ValueError("ws must be contiguous")
+    xs, os_ = x.stride(), out.stride()
+    if (cols > 1 and xs[1] != 1) or (osh[1] > 1 and os_[1] != 1):
+        raise ValueError("rows of x and out must be contiguous (stride 1 along the last dim)")
+    amax_p = 0
     if amax_out is not None:
         _need(amax_out, "amax_out", dtype=torch.float32, min_numel=1)
+        amax_p = amax_out.data_ptr()
     cx, cw = xq.c(), w.c()
-    _check(_lib().nvfp4_linear(_ptr(x), _dtype_code(x), rows, cols, _ld(x), ctypes.byref(cw), ctypes.byref(cx),
-                               _ptr(out), _dtype_code(out), _ld(out), epilogue, _ptr(amax_out), _ptr(ws),
-                               ws.numel() * 4, _stream(stream)), "nvfp4_linear")
+    st = (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+    status = _lib().nvfp4_linear(x.data_ptr(), _dtype_code(x), rows, cols, xs[0] if rows > 1 else cols,
+                                 ctypes.byref(cw), ctypes.byref(cx), out.data_ptr(), _dtype_code(out),
+                                 os_[0] if rows > 1 else osh[1], epilogue, amax_p, ws.data_ptr(),
+                                 ws.numel() * ws.element_size(), st)
+    if status:
+        _check(status, "nvfp4_linear")
     return out
 
 
