@@ -315,7 +315,7 @@ def test_full_attn_proj_operands(nv):
 
 
 @pytest.mark.parametrize("shape,fb", [((12, 5, 3, 32), 8), ((9, 7, 2, 128), 4), ((3, 11, 4, 64), 8),
-                                      ((17, 2, 1, 16), 5), ((4, 40, 3, 128), 1)])
+                                      ((17, 2, 1, 16), 5), ((4, 40, 3, 128), 1), ((5, 1, 1, 16), 2)])
 @pytest.mark.parametrize("fo6", [False, True])
 def test_kv_quant_pair_small(nv, shape, fb, fo6):
     """K and V through nvfp4_kv_quant_pair (one amax and one encode launch for

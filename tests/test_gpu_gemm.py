@@ -497,3 +497,32 @@ def test_train_linear_triple_full(nv):
                                (dw, r["dw"], r["bdw"], False, "weight gradient")):
         worst = assert_gemm_close(gpu.float().cpu().numpy(), c, b, bf, tag)
         log(f"  {tag}: all rows within bound, max err/bound {worst:.3e}")
+
+
+@pytest.mark.parametrize("m,n,k,xdt,stride", [(1, 40, 16, "f32", 0), (1, 256, 512, "bf16", 0), (7, 33, 48, "bf16", 64),
+                                              (130, 96, 272, "f32", 288)])
+def test_linear_edges_against_oracle(nv, m, n, k, xdt, stride):
+    """nvfp4_linear on a single row (its leading dimension is taken from the
+    row length), K = 16 and other K below 512 (the bounds-checked GEMM path),
+    and activations given as a strided view (ld > K): codes bit-exact and
+    every output within the GEMM bound of the oracle."""
+    log(f"linear edge {m}x{n}x{k} {xdt} ld {stride or k}")
+    rng = np.random.default_rng(31 * m + n + k)
+    a = (rng.standard_normal((m, k)) * 2).astype(np.float32)
+    b = (rng.standard_normal((n, k)) * 0.05).astype(np.float32)
+    full = np.zeros((m, stride), np.float32) if stride else a
+    if stride:
+        full[:, :k] = a
+    xd = dev_f32(full)[:, :k] if stride else dev_f32(a)
+    if xdt == "bf16":
+        a = widen(workloads.to_bf16_bits(a))
+        xd = xd.to(torch.bfloat16)
+    gw = nv.quantize(dev_f32(b))
+    xq = nv.NVFP4Tensor.empty(m, k, 1, "cuda")
+    y = nv.linear(xd, gw, out_dtype=torch.float32, xq=xq)
+    oa, ob = oracle.quantize(a), oracle.quantize(b)
+    torch.cuda.synchronize()
+    assert_q_exact(xq, oa, "linear's activation operand")
+    assert_q_exact(gw, ob, "W")
+    cref, bound = oracle.gemm_ref(oa, ob)
+    assert_gemm_close(y.cpu().numpy(), cref, bound, False, f"linear {m}x{n}x{k}")
